@@ -1,0 +1,224 @@
+"""Seeded synthetic inputs for paged single-token decode attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic and none of the kernels' address code. It serves both the
+HIP path (as device tensors) and the CPU oracle (whose inputs are the logical,
+unpaged K/V drawn here).
+
+Recipe (fixed draw order on one ``torch.Generator`` seeded per workload):
+  1. seq_lens (when the workload draws them),
+  2. q [S, 24, 256], 3. logical K [sum L, 4, 256], 4. logical V,
+  5. a permutation of the physical page pool.
+Values are fp32 N(0, 1) rounded to bf16 (round-to-nearest-even), times an
+exact power-of-two factor where the workload says so. Sequence s owns the next
+ceil(L_s / B) ids of the permutation, so sequences interleave physically.
+Every pool slot that holds no valid token is NaN (bf16 0x7FC0), and block-table
+entries past a sequence's last page point at one extra all-NaN page.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+HQ, HKV, HEAD = 24, 4, 256
+NAN_BF16 = 0x7FC0
+
+
+@dataclass
+class Case:
+    name: str
+    seed: int
+    q: torch.Tensor              # [S, HQ, HEAD] bf16
+    k_logical: torch.Tensor      # [sum L, HKV, HEAD] bf16 (sequences back to back)
+    v_logical: torch.Tensor
+    lens: list                   # host copy of seq_lens
+    seq_lens: torch.Tensor       # [S] int32
+    block_table: torch.Tensor    # [S, max_blocks] int32
+    k_cache: torch.Tensor        # [pool + 1, B, HKV, HEAD] bf16; page `pool` is the NaN pad
+    v_cache: torch.Tensor
+    block_size: int
+    scale: float
+    partition_tokens: int = 0    # 0 = let the library choose
+    pool_pages: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.lens)
+
+    @property
+    def max_seq_len(self) -> int:
+        return max(self.lens) if self.lens else 0
+
+    def cu(self, s: int) -> tuple:
+        lo = sum(self.lens[:s])
+        return lo, lo + self.lens[s]
+
+    def keys(self, s: int) -> torch.Tensor:
+        lo, hi = self.cu(s)
+        return self.k_logical[lo:hi]
+
+    def values(self, s: int) -> torch.Tensor:
+        lo, hi = self.cu(s)
+        return self.v_logical[lo:hi]
+
+    def algorithmic_bytes(self) -> int:
+        """K and V rows of every valid token plus Q, in bytes."""
+        return sum(self.lens) * HKV * HEAD * 2 * 2 + self.num_seqs * HQ * HEAD * 2
+
+
+# name -> (description, builder kwargs). Sizes follow the five workloads of the
+# decode microbenchmark study: tiny, single long sequence at page832, the
+# page784/page832 A/B, a batched long-context mix and a wide serving batch.
+WORKLOADS = {
+    "tiny_l1024_b64": dict(lens=[1024], block_size=64, pool_pages=32, seed=1),
+    "long_l8192_b832": dict(lens=[8192], block_size=832, pool_pages=64, seed=2),
+    "long_l16384_b832": dict(lens=[16384], block_size=832, pool_pages=64, seed=2),
+    "long_l32768_b832": dict(lens=[32768], block_size=832, pool_pages=64, seed=2),
+    "ab_l32768_b784": dict(lens=[32768], block_size=784, pool_pages=64, seed=3),
+    "ab_l32768_b832": dict(lens=[32768], block_size=832, pool_pages=64, seed=3),
+    "batched_8seq_t131072_b832": dict(lens="split131072", block_size=832,
+                                      pool_pages=200, seed=4, value_scale=0.5),
+    "wide_64seq_b832_p4096": dict(lens="uniform2048_65536", block_size=832,
+                                  pool_pages="fit110", seed=5, partition_tokens=4096),
+}
+
+
+def _draw_lens(spec, gen, device):
+    if spec == "split131072":
+        # 8 sequences, each 4096 + one gap of 7 sorted uniform cut points over
+        # 131072 - 8 * 4096 tokens, so the lengths add up to 131072.
+        free = 131072 - 8 * 4096
+        cuts = torch.randint(0, free + 1, (7,), generator=gen, device=device)
+        cuts = sorted(int(c) for c in cuts.cpu())
+        edges = [0] + cuts + [free]
+        return [4096 + edges[i + 1] - edges[i] for i in range(8)]
+    if spec == "uniform2048_65536":
+        lens = torch.randint(2048, 65536 + 1, (64,), generator=gen, device=device)
+        return [int(x) for x in lens.cpu()]
+    return list(spec)
+
+
+def _normal_bf16(shape, gen, device, value_scale):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    x = x.to(torch.bfloat16)
+    if value_scale != 1.0:
+        x = x * value_scale          # power of two: exact in bf16
+    return x
+
+
+def build_case(name, lens, block_size, pool_pages=None, seed=0, value_scale=1.0,
+               partition_tokens=0, scale=1.0 / 16.0, gen_device="cpu",
+               device="cpu", joint_kv=False):
+    """Draw one workload and lay it out in a NaN-poisoned paged pool.
+
+    joint_kv=True stores K and V in one [pool + 1, 2, B, HKV, HEAD] tensor and
+    returns the two unbind views (page stride 2 * B * HKV * HEAD).
+    """
+    gen = torch.Generator(device=gen_device)
+    gen.manual_seed(seed)
+    lens = _draw_lens(lens, gen, gen_device)
+    n_seq = len(lens)
+    bsz = int(block_size)
+    pages_per_seq = [-(-length // bsz) for length in lens]
+    if pool_pages == "fit110":
+        pool_pages = math.ceil(1.1 * sum(pages_per_seq))
+    if pool_pages is None:
+        pool_pages = sum(pages_per_seq) + 3
+    assert pool_pages >= sum(pages_per_seq), "pool too small"
+
+    q = _normal_bf16((n_seq, HQ, HEAD), gen, gen_device, value_scale)
+    total = sum(lens)
+    k_log = _normal_bf16((total, HKV, HEAD), gen, gen_device, value_scale)
+    v_log = _normal_bf16((total, HKV, HEAD), gen, gen_device, value_scale)
+    perm = torch.randperm(pool_pages, generator=gen, device=gen_device).cpu().tolist()
+
+    max_blocks = max(1, max(pages_per_seq) if pages_per_seq else 1)
+    pad_page = pool_pages
+    table = torch.full((n_seq, max_blocks), pad_page, dtype=torch.int32)
+    nxt = 0
+    for s, n in enumerate(pages_per_seq):
+        table[s, :n] = torch.tensor(perm[nxt:nxt + n], dtype=torch.int32)
+        nxt += n
+
+    shape = (pool_pages + 1, bsz, HKV, HEAD)
+    nan = torch.tensor(NAN_BF16, dtype=torch.int16).view(torch.bfloat16)
+    if joint_kv:
+        joint = torch.empty((pool_pages + 1, 2, bsz, HKV, HEAD), dtype=torch.bfloat16,
+                            device=device)
+        joint.fill_(float(nan))
+        k_cache, v_cache = joint.unbind(1)
+    else:
+        k_cache = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        v_cache = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        k_cache.fill_(float(nan))
+        v_cache.fill_(float(nan))
+
+    k_dev = k_log.to(device)
+    v_dev = v_log.to(device)
+    base = 0
+    for s, length in enumerate(lens):
+        for lp in range(pages_per_seq[s]):
+            lo = lp * bsz
+            hi = min(lo + bsz, length)
+            pp = int(table[s, lp])
+            k_cache[pp, : hi - lo] = k_dev[base + lo: base + hi]
+            v_cache[pp, : hi - lo] = v_dev[base + lo: base + hi]
+        base += length
+
+    return Case(
+        name=name, seed=seed, q=q.to(device), k_logical=k_dev, v_logical=v_dev,
+        lens=lens, seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
+        block_table=table.to(device), k_cache=k_cache, v_cache=v_cache,
+        block_size=bsz, scale=scale, partition_tokens=partition_tokens,
+        pool_pages=pool_pages,
+    )
+
+
+def make_case(name, device="cpu", gen_device=None, seed=None, **over):
+    """Build a named workload. The wide batch draws on the device generator
+    (about 2 x 2.2 G values); all others draw on the CPU generator."""
+    spec = dict(WORKLOADS[name])
+    if seed is not None:
+        spec["seed"] = seed
+    if gen_device is None:
+        gen_device = device if name.startswith("wide") else "cpu"
+    spec.update(over)
+    return build_case(name, gen_device=gen_device, device=device, **spec)
+
+
+def replicate(case: Case, copies: int):
+    """Cold-cache replicas: ``copies`` disjoint copies of every used page in one
+    pool, with one block table per copy ([copies, S, max_blocks]).
+
+    Replica r's pages are r * pool + the original ids; the last page of the
+    new pool is the NaN pad target. Each copy holds the same tokens, so every
+    replica gives the same attention result.
+    """
+    pool = case.pool_pages
+    bsz = case.block_size
+    dev = case.k_cache.device
+    shape = (copies * pool + 1, bsz, HKV, HEAD)
+    k_big = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    v_big = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    nan = torch.tensor(NAN_BF16, dtype=torch.int16).view(torch.bfloat16)
+    k_big.fill_(float(nan))
+    v_big.fill_(float(nan))
+    table = case.block_table.cpu()
+    used = sorted({int(x) for s in range(case.num_seqs)
+                   for x in table[s, : -(-case.lens[s] // bsz)].tolist()})
+    used_t = torch.tensor(used, dtype=torch.long, device=dev)
+    tables = []
+    for r in range(copies):
+        k_big[used_t + r * pool] = case.k_cache[used_t]
+        v_big[used_t + r * pool] = case.v_cache[used_t]
+        t = table.clone()
+        for s in range(case.num_seqs):
+            n = -(-case.lens[s] // bsz)
+            t[s, :n] += r * pool
+            t[s, n:] = copies * pool
+        tables.append(t)
+    return k_big, v_big, torch.stack(tables).to(dev)
