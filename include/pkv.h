@@ -1,0 +1,189 @@
+/*
+ * pkv.h -- single-token decode attention over a paged KV cache, for AMD
+ * MI355X (gfx950). C ABI; every call is asynchronous on the caller's stream.
+ *
+ * What is computed. For every sequence s and query head h (KV head g = h / G,
+ * G = num_q_heads / num_kv_heads = 6):
+ *     s_t = scale * q[s,h,:] . K_s[t,g,:]            for t < seq_lens[s]
+ *     o[s,h,:] = sum_t softmax(s)_t V_s[t,g,:]
+ * ("From Attention to KV Cache Compression: Notes from a KernelGen
+ * Optimization", "Starting from Attention": dot-product attention and the
+ * decode step that attends to every cached token). K_s / V_s row t is read
+ * through the block table: logical page t / block_size, offset t %
+ * block_size, physical page block_table[s, logical page] ("海光 DCU 上的长上下文
+ * Attention：从 page784 到 page832 的 KV Cache 对齐与访存优化", §1; page shape
+ * [block_size, 4, 256] per K or V page, §4; both page784 and page832
+ * supported, §2 and §7).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory (HBM) on
+ *    the current HIP device; `params` / `info` are host pointers.
+ *  - bf16 values are passed as raw 16-bit storage (`void*` / uint16_t).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Nothing here
+ *    synchronizes the stream or the device.
+ *  - The caller owns and allocates every buffer; the library allocates no
+ *    device memory and keeps no state besides an immutable per-process log
+ *    flag, so calls are thread-safe.
+ *  - Host-side checks run before any launch and return a negative status;
+ *    a failed launch returns PKV_ERR_HIP. Nothing is written on error.
+ *  - Preconditions that live in device memory are documented, not checked:
+ *    0 <= seq_lens[s] <= max_seq_len <= max_blocks_per_seq * block_size;
+ *    block_table[s, j] for j < ceil(seq_lens[s] / block_size) is a valid page
+ *    index of both caches; outputs alias no input.
+ *  - seq_lens[s] == 0 writes a zero output row (lse = -inf in partials).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL or misaligned           */
+  PKV_ERR_SHAPE = -2,       /* head counts / sizes / table width inconsistent     */
+  PKV_ERR_BLOCK_SIZE = -3,  /* block_size not a positive multiple of 16           */
+  PKV_ERR_PARTITION = -4,   /* partition_tokens not 0 and not a multiple of 64    */
+  PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+  PKV_ERR_UNSUPPORTED = -6, /* head_size != 256 or group size != 6                */
+  PKV_ERR_HIP = -7,         /* a HIP launch or runtime call failed                */
+  PKV_ERR_STRIDE = -8       /* page stride too small or not a multiple of 8       */
+} pkv_status;
+
+/* Geometry of one decode call. All sizes in elements unless noted. */
+typedef struct {
+  int32_t num_seqs;           /* S >= 0                                             */
+  int32_t num_q_heads;        /* Hq = 6 * Hkv (24 for the 24/4 layout)              */
+  int32_t num_kv_heads;       /* Hkv >= 1 (4)                                       */
+  int32_t head_size;          /* D, must be 256                                     */
+  int32_t block_size;         /* B: tokens per physical page, multiple of 16
+                                 (784 and 832 are the page sizes of the study)     */
+  int32_t max_blocks_per_seq; /* row stride of block_table, in int32 elements       */
+  int64_t k_page_stride;      /* elements between consecutive physical K pages:
+                                 B*Hkv*D for a [pages,B,Hkv,D] tensor, 2*B*Hkv*D
+                                 for the unbind(1) view of [pages,2,B,Hkv,D]        */
+  int64_t v_page_stride;      /* same for the V cache                               */
+  int32_t max_seq_len;        /* host-known upper bound on seq_lens (grid planning) */
+  int32_t partition_tokens;   /* split-KV partition P: 0 = choose automatically,
+                                 else a multiple of 64                              */
+  float scale;                /* softmax scale (1/sqrt(256) = 1/16 for D = 256)     */
+} pkv_decode_params;
+
+/* What a call with these params will launch (host-only query, no GPU use). */
+typedef struct {
+  int32_t partition_tokens;      /* P in use                                       */
+  int32_t num_partitions;        /* ceil(max_seq_len / P), at least 1              */
+  int32_t split_workgroups;      /* S * Hkv * num_partitions                       */
+  int32_t combine_workgroups;    /* S * Hq, or 0 when one partition covers all     */
+  int32_t full_groups_per_page;  /* block_size / 64 (12 for 784, 13 for 832)       */
+  int32_t tail_tokens_per_page;  /* block_size % 64 (16 for 784, 0 for 832)        */
+  int64_t workspace_bytes;       /* what pkv_decode needs in `workspace`           */
+} pkv_plan_info;
+
+/* Library version string (static storage). */
+PKV_API const char* pkv_version(void);
+
+/* Human-readable name of a pkv_status value (static storage). */
+PKV_API const char* pkv_status_string(int status);
+
+/* Validate params and report the launch plan. Host only; never touches a GPU.
+ * Returns the same status pkv_decode would return for these params. */
+PKV_API pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info);
+
+/* Bytes of device workspace pkv_decode needs for these params (0 when one
+ * partition covers every sequence, or when params are invalid). The
+ * workspace holds fp32 per-partition outputs and log-sum-exps. */
+PKV_API size_t pkv_decode_workspace_bytes(const pkv_decode_params* params);
+
+/* Decode attention. Device inputs:
+ *   q            bf16 [S, Hq, D], contiguous, 16-byte aligned
+ *   key_cache    bf16 pages: page p starts at key_cache + p * k_page_stride and
+ *                holds [B, Hkv, D] contiguous; 16-byte aligned
+ *   value_cache  same with v_page_stride
+ *   block_table  int32 [S, max_blocks_per_seq]
+ *   seq_lens     int32 [S]
+ * Device output:
+ *   out          bf16 [S, Hq, D], round-to-nearest-even from fp32
+ * Workspace: device memory of at least pkv_decode_workspace_bytes(params)
+ * bytes, 256-byte aligned (may be NULL when that is 0); contents on entry are
+ * ignored and clobbered. Launches the split-KV partition kernel and, when more
+ * than one partition is planned, the log-sum-exp combine kernel. */
+PKV_API pkv_status pkv_decode(const pkv_decode_params* params, const void* q,
+                      const void* key_cache, const void* value_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Same computation with the intermediate fp32 results exposed (for checks):
+ *   o_partial   fp32 [S, Hq, num_partitions, D]: partition p of sequence s is
+ *               softmax attention over tokens [p*P, min((p+1)*P, L_s)),
+ *               written for p < ceil(L_s / P) only
+ *   lse_partial fp32 [S, Hq, num_partitions]: natural-log log-sum-exp of the
+ *               scaled scores of that partition
+ *   out_f32     fp32 [S, Hq, D]: the combined output before the bf16 cast
+ *   out         bf16 [S, Hq, D] (may be NULL)
+ * num_partitions comes from pkv_plan. Always runs split + combine. */
+PKV_API pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
+                               const void* key_cache, const void* value_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               float* o_partial, float* lse_partial,
+                               float* out_f32, void* out, void* stream);
+
+/* The split-KV partition kernel on its own: writes o_partial / lse_partial
+ * (layout as in pkv_decode_partials, P and num_partitions from pkv_plan) for
+ * every p < ceil(L_s / P); pkv_split followed by pkv_combine computes what
+ * pkv_decode computes. */
+PKV_API pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void* key_cache,
+                     const void* value_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, float* o_partial, float* lse_partial,
+                     void* stream);
+
+/* The log-sum-exp combine on its own: merges partitions of size P (from
+ * pkv_plan(params)) laid out as in pkv_decode_partials into out (bf16,
+ * may be NULL) and out_f32 (may be NULL). */
+PKV_API pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,
+                       const float* lse_partial, const int32_t* seq_lens,
+                       void* out, float* out_f32, void* stream);
+
+/* Test/debug: the element offset that the decode kernel's page walker computes
+ * for every token of KV head kv_head, through the key-cache geometry
+ * (k_page_stride). row_offsets int64 [S, max_seq_len]; entries at t >=
+ * seq_lens[s] are set to -1. Uses the same partition / wave / block walk as
+ * pkv_decode with the planned P. */
+PKV_API pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int64_t* row_offsets, void* stream);
+
+/* Test/debug: copy every valid token row of `cache` (key-cache geometry,
+ * k_page_stride) into dense bf16 [S, max_seq_len, Hkv, D] through the decode
+ * kernel's page walker and tile loaders (K-operand and V-operand lane
+ * layouts both exercised: which = 0 uses the K loader, 1 the V loader).
+ * Rows at t >= seq_lens[s] are left untouched. */
+PKV_API pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which,
+                            const void* cache, const int32_t* block_table,
+                            const int32_t* seq_lens, void* dense, void* stream);
+
+/* Bandwidth probes (used to calibrate measurements, not part of decode):
+ * pkv_probe_read streams `bytes` (multiple of 16, 16-byte aligned) from `buf`
+ * and writes one float per workgroup sum into `sink` (device, at least
+ * pkv_probe_sink_floats() floats); pkv_probe_copy copies `bytes` (multiple
+ * of 16, both 16-byte aligned). */
+PKV_API int32_t pkv_probe_sink_floats(void);
+PKV_API pkv_status pkv_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
+PKV_API pkv_status pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,1 +1,22 @@
-"""Paged KV-cache single-token decode attention for AMD MI355X (gfx950)."""
+"""Paged KV-cache single-token decode attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
+``paged_kv_cache_36_amd.api`` is its thin Python binding. ``synth`` draws the
+seeded synthetic inputs.
+"""
+
+from ._lib import LIB_PATH, LibraryMissing, load  # noqa: F401
+from .api import (  # noqa: F401
+    PkvError,
+    combine,
+    debug_gather,
+    debug_resolve,
+    decode,
+    decode_partials,
+    make_params,
+    plan,
+    probe_copy,
+    probe_read,
+    split,
+    workspace_bytes,
+)

@@ -1,0 +1,87 @@
+"""ctypes loader for the in-tree HIP library ``libpkv.so``.
+
+Argument marshalling only: no computation happens in Python. Importing this
+module never falls back to anything; if the library is missing, every call
+raises ``LibraryMissing``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("k_page_stride", ctypes.c_int64),
+        ("v_page_stride", ctypes.c_int64),
+        ("max_seq_len", ctypes.c_int32),
+        ("partition_tokens", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("partition_tokens", ctypes.c_int32),
+        ("num_partitions", ctypes.c_int32),
+        ("split_workgroups", ctypes.c_int32),
+        ("combine_workgroups", ctypes.c_int32),
+        ("full_groups_per_page", ctypes.c_int32),
+        ("tail_tokens_per_page", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.POINTER(DecodeParams)
+_VP = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+# symbol -> (restype, argtypes); every function declared in include/pkv.h
+SIGNATURES = {
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_plan": (_I32, [_P, ctypes.POINTER(PlanInfo)]),
+    "pkv_decode_workspace_bytes": (_SZ, [_P]),
+    "pkv_decode": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "pkv_decode_partials": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_split": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_combine": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_debug_resolve": (_I32, [_P, _I32, _VP, _VP, _VP, _VP]),
+    "pkv_debug_gather": (_I32, [_P, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_probe_sink_floats": (_I32, []),
+    "pkv_probe_read": (_I32, [_VP, _SZ, _VP, _VP]),
+    "pkv_probe_copy": (_I32, [_VP, _VP, _SZ, _VP]),
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpkv.so once; raise LibraryMissing if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                f"{LIB_PATH} is not built; run `python -m paged_kv_cache_36_amd.build` "
+                "(or __graft_entry__.build()) first. There is no fallback path.")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

@@ -1,0 +1,202 @@
+"""Python binding of the pkv C ABI (include/pkv.h), same names without the prefix.
+
+Argument marshalling only: tensors are checked for dtype/device/layout, their
+device pointers and strides are packed into ``pkv_decode_params`` and the C
+entry point is called on torch's current stream (or the one given). Every
+step of the computation runs in the HIP kernels of ``libpkv.so``; there is no
+Python or CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import DecodeParams, PlanInfo, load
+
+HEAD_SIZE = 256
+GROUP = 6
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = load().pkv_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PkvError(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+
+
+def _page_stride(cache: torch.Tensor, name: str) -> int:
+    """[pages, B, Hkv, D] with each page contiguous; pages may be spaced (unbind view)."""
+    _need(cache, name, torch.bfloat16, 4)
+    _, b, hkv, d = cache.shape
+    if cache.stride(3) != 1 or cache.stride(2) != d or cache.stride(1) != hkv * d:
+        raise ValueError(f"{name}: each page must be a contiguous [B, Hkv, D] block, "
+                         f"got strides {cache.stride()}")
+    return cache.stride(0)
+
+
+def make_params(q, key_cache, value_cache, block_table, block_size, scale,
+                max_seq_len=None, partition_tokens=0) -> DecodeParams:
+    _need(q, "q", torch.bfloat16, 3)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [S, Hq, D]")
+    ks = _page_stride(key_cache, "key_cache")
+    vs = _page_stride(value_cache, "value_cache")
+    if key_cache.shape[1:] != value_cache.shape[1:]:
+        raise ValueError("key_cache and value_cache pages differ in shape")
+    if key_cache.shape[1] != block_size:
+        raise ValueError(f"cache pages hold {key_cache.shape[1]} tokens, block_size={block_size}")
+    _need(block_table, "block_table", torch.int32, 2)
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous [S, max_blocks]")
+    s, hq, d = q.shape
+    if block_table.shape[0] != s:
+        raise ValueError("block_table rows != number of sequences")
+    hkv = key_cache.shape[2]
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * block_size
+    p = DecodeParams()
+    p.num_seqs = s
+    p.num_q_heads = hq
+    p.num_kv_heads = hkv
+    p.head_size = d
+    p.block_size = int(block_size)
+    p.max_blocks_per_seq = block_table.shape[1]
+    p.k_page_stride = ks
+    p.v_page_stride = vs
+    p.max_seq_len = int(max_seq_len)
+    p.partition_tokens = int(partition_tokens)
+    p.scale = float(scale)
+    return p
+
+
+def plan(params: DecodeParams) -> dict:
+    info = PlanInfo()
+    _check(load().pkv_plan(ctypes.byref(params), ctypes.byref(info)), "pkv_plan")
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def workspace_bytes(params: DecodeParams) -> int:
+    return int(load().pkv_decode_workspace_bytes(ctypes.byref(params)))
+
+
+def _seq_lens(seq_lens, s):
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.shape[0] != s or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be contiguous int32 [S]")
+
+
+def decode(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, *,
+           max_seq_len=None, partition_tokens=0, out=None, workspace=None, stream=None):
+    """o = softmax(q K^T * scale) V per sequence, K/V read through block_table.
+
+    Returns ``out`` (bf16 [S, Hq, D]); allocates it (and the workspace) with
+    torch when not given.
+    """
+    p = make_params(q, key_cache, value_cache, block_table, block_size, scale,
+                    max_seq_len, partition_tokens)
+    _seq_lens(seq_lens, q.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_bytes(p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pkv_decode(ctypes.byref(p), _ptr(q), _ptr(key_cache), _ptr(value_cache),
+                             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(workspace),
+                             ws_bytes, _stream(stream)), "pkv_decode")
+    return out
+
+
+def decode_partials(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, *,
+                    max_seq_len=None, partition_tokens=0, stream=None):
+    """Returns (o_partial [S,Hq,n,D] f32, lse_partial [S,Hq,n] f32, out_f32 [S,Hq,D], out bf16)."""
+    p = make_params(q, key_cache, value_cache, block_table, block_size, scale,
+                    max_seq_len, partition_tokens)
+    _seq_lens(seq_lens, q.shape[0])
+    n = plan(p)["num_partitions"]
+    s, hq, d = q.shape
+    o_part = torch.zeros((s, hq, n, d), dtype=torch.float32, device=q.device)
+    lse_part = torch.full((s, hq, n), float("nan"), dtype=torch.float32, device=q.device)
+    out_f32 = torch.empty((s, hq, d), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+    _check(load().pkv_decode_partials(ctypes.byref(p), _ptr(q), _ptr(key_cache),
+                                      _ptr(value_cache), _ptr(block_table), _ptr(seq_lens),
+                                      _ptr(o_part), _ptr(lse_part), _ptr(out_f32), _ptr(out),
+                                      _stream(stream)), "pkv_decode_partials")
+    return o_part, lse_part, out_f32, out
+
+
+def split(params: DecodeParams, q, key_cache, value_cache, block_table, seq_lens, o_partial,
+          lse_partial, stream=None):
+    """The split-KV partition kernel alone (fp32 partials into caller buffers)."""
+    _check(load().pkv_split(ctypes.byref(params), _ptr(q), _ptr(key_cache), _ptr(value_cache),
+                            _ptr(block_table), _ptr(seq_lens), _ptr(o_partial),
+                            _ptr(lse_partial), _stream(stream)), "pkv_split")
+
+
+def combine(params: DecodeParams, o_partial, lse_partial, seq_lens, *, out=None, out_f32=None,
+            stream=None):
+    _check(load().pkv_combine(ctypes.byref(params), _ptr(o_partial), _ptr(lse_partial),
+                              _ptr(seq_lens), _ptr(out), _ptr(out_f32), _stream(stream)),
+           "pkv_combine")
+    return out, out_f32
+
+
+def debug_resolve(params: DecodeParams, kv_head, block_table, seq_lens, stream=None):
+    offs = torch.empty((params.num_seqs, params.max_seq_len), dtype=torch.int64,
+                       device=block_table.device)
+    _check(load().pkv_debug_resolve(ctypes.byref(params), int(kv_head), _ptr(block_table),
+                                    _ptr(seq_lens), _ptr(offs), _stream(stream)),
+           "pkv_debug_resolve")
+    return offs
+
+
+def debug_gather(params: DecodeParams, which, cache, block_table, seq_lens, fill=0, stream=None):
+    dense = torch.full((params.num_seqs, params.max_seq_len, params.num_kv_heads, HEAD_SIZE),
+                       fill, dtype=torch.int16, device=cache.device).view(torch.bfloat16)
+    _check(load().pkv_debug_gather(ctypes.byref(params), int(which), _ptr(cache),
+                                   _ptr(block_table), _ptr(seq_lens), _ptr(dense),
+                                   _stream(stream)), "pkv_debug_gather")
+    return dense
+
+
+def probe_sink_floats() -> int:
+    return int(load().pkv_probe_sink_floats())
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    _check(load().pkv_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(stream)), "pkv_probe_read")
+
+
+def probe_copy(dst: torch.Tensor, src: torch.Tensor, stream=None):
+    _check(load().pkv_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                                 _stream(stream)), "pkv_probe_copy")

@@ -1,0 +1,318 @@
+// C-ABI host layer: argument validation, split-KV planning, launch.
+// Declarations and the contract of every entry point are in include/pkv.h.
+
+#include "pkv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "pkv_launch.h"
+
+namespace {
+
+constexpr int64_t kAutoTargetWorkgroups = 1024;  // about 4 per CU on 256 CUs
+constexpr int32_t kAutoMinPartition = 64;
+constexpr int32_t kAutoMaxPartition = 4096;
+constexpr size_t kWorkspaceAlign = 256;
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("PKV_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int32_t P = 0;
+  int32_t n_parts = 0;
+  size_t o_part_bytes = 0;
+  size_t workspace = 0;
+};
+
+// Geometry checks that need no pointers.
+pkv_status check_params(const pkv_decode_params* p) {
+  if (p == nullptr) return PKV_ERR_NULL;
+  if (p->num_seqs < 0 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_seq_len < 0 ||
+      p->max_blocks_per_seq < 1)
+    return PKV_ERR_SHAPE;
+  if (p->head_size != pkv::kHeadSize) return PKV_ERR_UNSUPPORTED;
+  if (p->num_q_heads != p->num_kv_heads * pkv::kGroup) return PKV_ERR_UNSUPPORTED;
+  if (p->num_kv_heads > 64) return PKV_ERR_SHAPE;
+  if (p->block_size < 16 || p->block_size % 16 != 0) return PKV_ERR_BLOCK_SIZE;
+  if (static_cast<int64_t>(p->max_seq_len) >
+      static_cast<int64_t>(p->max_blocks_per_seq) * p->block_size)
+    return PKV_ERR_SHAPE;
+  const int64_t page_elems = static_cast<int64_t>(p->block_size) * p->num_kv_heads * p->head_size;
+  if (p->k_page_stride < page_elems || p->v_page_stride < page_elems || p->k_page_stride % 8 != 0 ||
+      p->v_page_stride % 8 != 0)
+    return PKV_ERR_STRIDE;
+  if (p->partition_tokens < 0 || p->partition_tokens % 64 != 0) return PKV_ERR_PARTITION;
+  if (!std::isfinite(p->scale)) return PKV_ERR_SHAPE;
+  return PKV_OK;
+}
+
+Plan make_plan(const pkv_decode_params* p) {
+  Plan pl;
+  int32_t P = p->partition_tokens;
+  if (P == 0) {
+    // Enough (sequence, KV head, partition) workgroups to give every CU a few,
+    // counting the longest sequence for every slot of the batch.
+    const int64_t token_heads =
+        static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * static_cast<int64_t>(p->max_seq_len);
+    int64_t want = (token_heads + kAutoTargetWorkgroups - 1) / kAutoTargetWorkgroups;
+    want = (want + 63) / 64 * 64;
+    if (want < kAutoMinPartition) want = kAutoMinPartition;
+    if (want > kAutoMaxPartition) want = kAutoMaxPartition;
+    P = static_cast<int32_t>(want);
+  }
+  pl.P = P;
+  pl.n_parts = p->max_seq_len > 0 ? (p->max_seq_len + P - 1) / P : 1;
+  if (pl.n_parts > 1) {
+    const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * pl.n_parts;
+    pl.o_part_bytes = round_up(rows * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
+    pl.workspace = pl.o_part_bytes + round_up(rows * sizeof(float), kWorkspaceAlign);
+  }
+  return pl;
+}
+
+pkv::LaunchArgs base_args(const pkv_decode_params* p, const Plan& pl) {
+  pkv::LaunchArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_page_stride = p->k_page_stride;
+  a.v_page_stride = p->v_page_stride;
+  a.num_seqs = p->num_seqs;
+  a.num_kv_heads = p->num_kv_heads;
+  a.block_size = p->block_size;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.partition_tokens = pl.P;
+  a.n_parts = pl.n_parts;
+  a.max_seq_len = p->max_seq_len;
+  a.scale_log2 = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
+  return a;
+}
+
+void log_plan(const char* what, const pkv_decode_params* p, const Plan& pl) {
+  if (!log_enabled()) return;
+  std::fprintf(stderr,
+               "[pkv] %s: S=%d Hq=%d Hkv=%d D=%d block_size=%d (64-token groups %d, tail %d) "
+               "max_seq_len=%d P=%d partitions=%d split_wg=%lld combine=%s workspace=%zu\n",
+               what, p->num_seqs, p->num_q_heads, p->num_kv_heads, p->head_size, p->block_size,
+               p->block_size / 64, p->block_size % 64, p->max_seq_len, pl.P, pl.n_parts,
+               static_cast<long long>(p->num_seqs) * p->num_kv_heads * pl.n_parts,
+               pl.n_parts > 1 ? "yes" : "no", pl.workspace);
+}
+
+pkv_status check_inputs(const void* q, const void* k, const void* v, const int32_t* bt,
+                        const int32_t* sl) {
+  if (!q || !k || !v || !bt || !sl) return PKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bt, 4) || !aligned(sl, 4))
+    return PKV_ERR_NULL;
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null or misaligned pointer";
+    case PKV_ERR_SHAPE: return "inconsistent shape";
+    case PKV_ERR_BLOCK_SIZE: return "block_size must be a positive multiple of 16";
+    case PKV_ERR_PARTITION: return "partition_tokens must be 0 or a multiple of 64";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_UNSUPPORTED: return "unsupported head geometry (need head_size 256, 6 query heads per KV head)";
+    case PKV_ERR_HIP: return "HIP launch or runtime error";
+    case PKV_ERR_STRIDE: return "page stride smaller than a page or not a multiple of 8";
+    default: return "unknown status";
+  }
+}
+
+pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (info == nullptr) return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  info->partition_tokens = pl.P;
+  info->num_partitions = pl.n_parts;
+  info->split_workgroups = params->num_seqs * params->num_kv_heads * pl.n_parts;
+  info->combine_workgroups = pl.n_parts > 1 ? params->num_seqs * params->num_q_heads : 0;
+  info->full_groups_per_page = params->block_size / 64;
+  info->tail_tokens_per_page = params->block_size % 64;
+  info->workspace_bytes = static_cast<int64_t>(pl.workspace);
+  return PKV_OK;
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_decode_params* params) {
+  if (check_params(params) != PKV_OK) return 0;
+  return make_plan(params).workspace;
+}
+
+pkv_status pkv_decode(const pkv_decode_params* params, const void* q, const void* key_cache,
+                      const void* value_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (params->num_seqs == 0) return PKV_OK;
+  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
+  if (st != PKV_OK) return st;
+  if (!out || !aligned(out, 16)) return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  if (pl.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < pl.workspace || !aligned(workspace, kWorkspaceAlign)))
+    return PKV_ERR_WORKSPACE;
+  log_plan("decode", params, pl);
+
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pl.n_parts == 1) return hip_status(pkv::launch_split(a, /*direct=*/true, s));
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.o_part_bytes);
+  st = hip_status(pkv::launch_split(a, /*direct=*/false, s));
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_combine(a, s));
+}
+
+pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
+                               const void* key_cache, const void* value_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               float* o_partial, float* lse_partial, float* out_f32, void* out,
+                               void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (params->num_seqs == 0) return PKV_OK;
+  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
+  if (st != PKV_OK) return st;
+  if (!o_partial || !lse_partial || !out_f32 || !aligned(o_partial, 16) || !aligned(out_f32, 16) ||
+      (out != nullptr && !aligned(out, 16)))
+    return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  log_plan("decode_partials", params, pl);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_split(a, /*direct=*/false, s));
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_combine(a, s));
+}
+
+pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void* key_cache,
+                     const void* value_cache, const int32_t* block_table,
+                     const int32_t* seq_lens, float* o_partial, float* lse_partial,
+                     void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (params->num_seqs == 0) return PKV_OK;
+  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
+  if (st != PKV_OK) return st;
+  if (!o_partial || !lse_partial || !aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  log_plan("split", params, pl);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  return hip_status(pkv::launch_split(a, /*direct=*/false, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,
+                       const float* lse_partial, const int32_t* seq_lens, void* out,
+                       float* out_f32, void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (params->num_seqs == 0) return PKV_OK;
+  if (!o_partial || !lse_partial || !seq_lens || !aligned(o_partial, 16) ||
+      (out != nullptr && !aligned(out, 16)) || (out_f32 != nullptr && !aligned(out_f32, 16)))
+    return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.seq_lens = seq_lens;
+  a.o_part = const_cast<float*>(o_partial);
+  a.lse_part = const_cast<float*>(lse_partial);
+  a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
+  return hip_status(pkv::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int64_t* row_offsets, void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (kv_head < 0 || kv_head >= params->num_kv_heads) return PKV_ERR_SHAPE;
+  if (params->num_seqs == 0) return PKV_OK;
+  if (!block_table || !seq_lens || !row_offsets || !aligned(row_offsets, 8)) return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  return hip_status(
+      pkv::launch_debug_resolve(a, kv_head, row_offsets, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which, const void* cache,
+                            const int32_t* block_table, const int32_t* seq_lens, void* dense,
+                            void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (which != 0 && which != 1) return PKV_ERR_SHAPE;
+  if (params->num_seqs == 0) return PKV_OK;
+  if (!cache || !block_table || !seq_lens || !dense || !aligned(cache, 16) || !aligned(dense, 16))
+    return PKV_ERR_NULL;
+  const Plan pl = make_plan(params);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.k = static_cast<const uint16_t*>(cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  return hip_status(pkv::launch_debug_gather(a, which, static_cast<uint16_t*>(dense),
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_probe_sink_floats(void) { return pkv::probe_sink_floats(); }
+
+pkv_status pkv_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || bytes % 16 != 0) return PKV_ERR_NULL;
+  return hip_status(pkv::launch_probe_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || !aligned(dst, 16) || !aligned(src, 16) || bytes % 16 != 0)
+    return PKV_ERR_NULL;
+  return hip_status(pkv::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

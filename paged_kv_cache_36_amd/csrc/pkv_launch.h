@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host layer (pkv_api.cpp) and the HIP
+// kernels (pkv_kernels.hip). Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kHeadSize = 256;   // D
+constexpr int kGroup = 6;        // query heads per KV head
+constexpr int kWaveTokens = 16;  // tokens one wave handles per step (MFMA rows)
+constexpr int kWaves = 4;        // waves per split workgroup
+constexpr int kTileTokens = kWaveTokens * kWaves;  // 64 tokens per workgroup step
+
+// Everything a split/combine/debug launch needs, already validated.
+struct LaunchArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint16_t* out;        // bf16 [S, Hq, D] or null
+  float* out_f32;       // fp32 [S, Hq, D] or null
+  float* o_part;        // fp32 [S, Hq, n_parts, D] or null
+  float* lse_part;      // fp32 [S, Hq, n_parts] or null
+  int64_t k_page_stride;
+  int64_t v_page_stride;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t partition_tokens;
+  int32_t n_parts;
+  int32_t max_seq_len;
+  float scale_log2;     // scale * log2(e)
+};
+
+// split kernel: per (sequence, KV head, partition). direct=true writes the
+// final bf16 (and optional fp32) output, valid only when n_parts == 1.
+hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream);
+hipError_t launch_combine(const LaunchArgs& a, hipStream_t stream);
+hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* offsets,
+                                hipStream_t stream);
+hipError_t launch_debug_gather(const LaunchArgs& a, int32_t which, uint16_t* dense,
+                               hipStream_t stream);
+int32_t probe_sink_floats();
+hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: symbols, host-side validation, planning."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_36_amd import _lib
+from paged_kv_cache_36_amd._lib import DecodeParams, PlanInfo
+from tests.conftest import ROOT, read_golden
+
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert "pkv_decode" in names and "pkv_debug_resolve" in names and len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.pkv_version()
+    for st in range(-8, 1):
+        assert lib.pkv_status_string(st) and lib.pkv_status_string(st) != b"unknown status"
+    assert lib.pkv_status_string(42) == b"unknown status"
+
+
+def params(**kw):
+    p = DecodeParams()
+    base = dict(num_seqs=1, num_q_heads=24, num_kv_heads=4, head_size=256, block_size=832,
+                max_blocks_per_seq=10, k_page_stride=832 * 1024, v_page_stride=832 * 1024,
+                max_seq_len=8192, partition_tokens=0, scale=1.0 / 16)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def plan(lib, **kw):
+    info = PlanInfo()
+    st = lib.pkv_plan(ctypes.byref(params(**kw)), ctypes.byref(info))
+    return st, info
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_size=128), -6),
+    (dict(num_q_heads=32), -6),
+    (dict(block_size=0), -3),
+    (dict(block_size=8), -3),
+    (dict(block_size=840), -3),
+    (dict(partition_tokens=100), -4),
+    (dict(partition_tokens=-64), -4),
+    (dict(max_seq_len=8321), -2),            # > max_blocks * block_size
+    (dict(k_page_stride=832 * 1024 - 8), -8),
+    (dict(v_page_stride=832 * 1024 + 4), -8),
+    (dict(num_seqs=-1), -2),
+    (dict(scale=float("inf")), -2),
+    (dict(num_kv_heads=0, num_q_heads=0), -2),
+])
+def test_plan_rejects_bad_params(lib, kw, status):
+    st, _ = plan(lib, **kw)
+    assert st == status
+
+
+def test_decode_validates_before_any_launch(lib):
+    # Every one of these returns from the host checks; no HIP call is reached.
+    p = params()
+    null = None
+    fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+    assert lib.pkv_decode(None, fake, fake, fake, fake, fake, fake, None, 0, None) == -1
+    assert lib.pkv_decode(ctypes.byref(p), null, fake, fake, fake, fake, fake, None, 0, None) == -1
+    mis = ctypes.c_void_p(0x10008)    # not 16-byte aligned
+    assert lib.pkv_decode(ctypes.byref(p), mis, fake, fake, fake, fake, fake, None, 0, None) == -1
+    # multi-partition plan without a workspace
+    assert lib.pkv_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, 0, None) == -5
+    need = lib.pkv_decode_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert lib.pkv_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, need - 1,
+                          None) == -5
+    bad = params(block_size=100)
+    assert lib.pkv_decode(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, need,
+                          None) == -3
+    # zero sequences is a no-op
+    assert lib.pkv_decode(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None,
+                          None, 0, None) == 0
+    assert lib.pkv_debug_resolve(ctypes.byref(p), 4, fake, fake, fake, None) == -2
+    assert lib.pkv_debug_gather(ctypes.byref(p), 2, fake, fake, fake, fake, None) == -2
+    assert lib.pkv_probe_read(fake, 17, fake, None) == -1
+    assert lib.pkv_probe_copy(fake, mis, 32, None) == -1
+
+
+def test_plan_page_geometry_matches_pages(lib):
+    for bsz, groups, tail, _pct, page_bytes in read_golden("page_geometry.txt"):
+        bsz = int(bsz)
+        st, info = plan(lib, block_size=bsz, k_page_stride=bsz * 1024, v_page_stride=bsz * 1024,
+                        max_blocks_per_seq=64, max_seq_len=bsz * 10)
+        assert st == 0
+        assert info.full_groups_per_page == int(groups)
+        assert info.tail_tokens_per_page == int(tail)
+        assert bsz * 4 * 256 * 2 == int(page_bytes)
+
+
+def test_capacity_overhead_matches_pages():
+    rows = {int(r[0]): float(r[3]) for r in read_golden("page_geometry.txt")}
+    for bsz in (832, 1024):
+        assert round(100.0 * (bsz - 784) / 784, 1) == rows[bsz]
+
+
+def test_plan_partitions_and_workspace(lib):
+    st, info = plan(lib, partition_tokens=4096, max_seq_len=8192)
+    assert st == 0
+    assert info.partition_tokens == 4096 and info.num_partitions == 2
+    assert info.split_workgroups == 1 * 4 * 2 and info.combine_workgroups == 24
+    rows = 1 * 24 * 2
+    assert info.workspace_bytes >= rows * 256 * 4 + rows * 4
+    # one partition: no combine, no workspace
+    st, info = plan(lib, partition_tokens=8192, max_seq_len=8192)
+    assert st == 0 and info.num_partitions == 1 and info.combine_workgroups == 0
+    assert info.workspace_bytes == 0
+    # auto partition is a multiple of 64 within [64, 4096]
+    for s, L in ((1, 8192), (8, 40000), (64, 65536), (1, 1)):
+        st, info = plan(lib, num_seqs=s, max_seq_len=L, max_blocks_per_seq=(L + 831) // 832)
+        assert st == 0
+        assert info.partition_tokens % 64 == 0 and 64 <= info.partition_tokens <= 4096
+        assert info.num_partitions == -(-L // info.partition_tokens)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()

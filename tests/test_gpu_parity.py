@@ -1,0 +1,243 @@
+"""HIP path vs the fp64 CPU oracle, through the C ABI (needs an MI355X)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_36_amd as pkv
+from oracle import decode as od
+from paged_kv_cache_36_amd import synth
+from tests.parity_util import (assert_bf16_close, assert_rows_rel, bits, f64, oracle_case)
+
+pytestmark = pytest.mark.gpu
+
+SWEEP_LENS = [1, 2, 63, 64, 65, 783, 784, 785, 831, 832, 833, 4095, 4096, 4097]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    pkv.load()   # raises if the HIP library is not built
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)}", flush=True)
+
+
+def run_decode(case, partition_tokens=None, **kw):
+    p_tok = case.partition_tokens if partition_tokens is None else partition_tokens
+    out = pkv.decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                     case.block_size, case.scale, partition_tokens=p_tok,
+                     max_seq_len=max(case.max_seq_len, 1), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def params_of(case, partition_tokens=0):
+    return pkv.make_params(case.q, case.k_cache, case.v_cache, case.block_table,
+                           case.block_size, case.scale, max(case.max_seq_len, 1),
+                           partition_tokens)
+
+
+# ------------------------------------------------------------ addressing (bit-exact)
+
+@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
+@pytest.mark.parametrize("ptok", [64, 256, 0])
+def test_resolver_offsets_bit_exact(bsz, ptok):
+    case = synth.build_case(f"res{bsz}", lens=[1, 63, 65, 785, 1700, 833], block_size=bsz,
+                            seed=11, device="cuda")
+    prm = params_of(case, ptok)
+    for g in range(4):
+        got = pkv.debug_resolve(prm, g, case.block_table, case.seq_lens).cpu().numpy()
+        ref = od.resolve_offsets(case.block_table.cpu().numpy(), case.lens, bsz,
+                                 case.k_cache.stride(0), 4, 256, g, case.max_seq_len)
+        assert np.array_equal(got, ref), (bsz, ptok, g)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
+def test_tile_loaders_gather_bit_exact(which, bsz):
+    case = synth.build_case(f"gat{bsz}", lens=[70, 1, 1600, 832], block_size=bsz, seed=12,
+                            device="cuda")
+    prm = params_of(case, 256)
+    sentinel = 0x1234
+    dense = pkv.debug_gather(prm, which, case.k_cache, case.block_table, case.seq_lens,
+                             fill=sentinel)
+    torch.cuda.synchronize()
+    d = bits(dense)
+    for s in range(case.num_seqs):
+        n = case.lens[s]
+        assert np.array_equal(d[s, :n], bits(case.keys(s))), (which, bsz, s)
+        assert np.all(d[s, n:] == sentinel)
+
+
+def test_joint_kv_unbind_view_addressing():
+    case = synth.build_case("joint", lens=[900, 33], block_size=832, seed=13, device="cuda",
+                            joint_kv=True)
+    assert case.k_cache.stride(0) == 2 * 832 * 1024
+    prm = params_of(case, 128)
+    dense = pkv.debug_gather(prm, 0, case.v_cache, case.block_table, case.seq_lens)
+    torch.cuda.synchronize()
+    for s in range(2):
+        assert np.array_equal(bits(dense)[s, :case.lens[s]], bits(case.values(s)))
+    out = run_decode(case, 128)
+    assert_bf16_close(out, oracle_case(case)[0], what="unbind view")
+
+
+# ------------------------------------------------------------ decode vs oracle
+
+def test_tiny_workload():
+    case = synth.make_case("tiny_l1024_b64", device="cuda")
+    ref, _ = oracle_case(case)
+    for ptok in (0, 64, 256, 1024):
+        print(f"[gpu] tiny P={ptok}", flush=True)
+        assert_bf16_close(run_decode(case, ptok), ref, what=f"tiny P={ptok}")
+
+
+@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
+def test_length_sweep(bsz):
+    case = synth.build_case(f"sweep{bsz}", lens=SWEEP_LENS, block_size=bsz, seed=21,
+                            device="cuda")
+    ref, _ = oracle_case(case)
+    for ptok in (0, 128, 4096):
+        print(f"[gpu] sweep B={bsz} P={ptok}", flush=True)
+        assert_bf16_close(run_decode(case, ptok), ref, what=f"sweep B={bsz} P={ptok}")
+
+
+def test_partials_and_fp32_output():
+    case = synth.build_case("parts", lens=[1, 300, 4097, 5000, 64], block_size=784, seed=31,
+                            device="cuda")
+    ptok = 1024
+    o_p, lse_p, out32, out = pkv.decode_partials(
+        case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens, case.block_size,
+        case.scale, partition_tokens=ptok, max_seq_len=case.max_seq_len)
+    torch.cuda.synchronize()
+    o_p, lse_p, out32 = f64(o_p), f64(lse_p), f64(out32)
+    q = f64(case.q)
+    worst = 0.0
+    for s in range(case.num_seqs):
+        k, v = f64(case.keys(s)), f64(case.values(s))
+        ref_p, ref_lse = od.decode_partials(q[s], k, v, case.scale, ptok)
+        n = ref_p.shape[1]
+        worst = max(worst, assert_rows_rel(o_p[s, :, :n], ref_p, what=f"o_partial s={s}"))
+        assert np.all(np.abs(lse_p[s, :, :n] - ref_lse) <= 1e-4 * np.maximum(1, np.abs(ref_lse)))
+        # partitions past the sequence are not written
+        assert np.all(o_p[s, :, n:] == 0) and np.all(np.isnan(lse_p[s, :, n:]))
+        ref_o, _ = od.attention_decode(q[s], k, v, case.scale)
+        assert_rows_rel(out32[s], ref_o, what=f"out_f32 s={s}")
+    assert_bf16_close(out, oracle_case(case)[0], what="partials bf16")
+    print(f"[gpu] worst fp32 partial row rel err {worst:.2e}", flush=True)
+
+
+def test_combine_entry_point_on_oracle_partials():
+    # The combine kernel alone, fed partials computed by the oracle.
+    case = synth.build_case("comb", lens=[700, 4097, 1], block_size=832, seed=32, device="cuda")
+    ptok = 512
+    prm = params_of(case, ptok)
+    n_max = pkv.plan(prm)["num_partitions"]
+    q = f64(case.q)
+    o_p = np.zeros((3, 24, n_max, 256))
+    lse_p = np.zeros((3, 24, n_max))
+    for s in range(3):
+        a, b = od.decode_partials(q[s], f64(case.keys(s)), f64(case.values(s)), case.scale, ptok)
+        o_p[s, :, :a.shape[1]] = a
+        lse_p[s, :, :a.shape[1]] = b
+    o_dev = torch.from_numpy(o_p).float().cuda()
+    lse_dev = torch.from_numpy(lse_p).float().cuda()
+    out = torch.empty_like(case.q)
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    pkv.combine(prm, o_dev, lse_dev, case.seq_lens, out=out, out_f32=out32)
+    torch.cuda.synchronize()
+    ref = oracle_case(case)[0]
+    for s in range(3):
+        assert_rows_rel(f64(out32)[s], ref[s], what=f"combine s={s}")
+    assert_bf16_close(out, ref, what="combine bf16")
+
+
+def test_invariant_to_page_size_and_permutation_bitwise():
+    outs = []
+    for bsz in (64, 784, 832):
+        for seed in (41, 42, 43):
+            # same logical tokens (drawn from seed 40), different pool permutations
+            base = synth.build_case("inv", lens=[3000, 1234], block_size=bsz, seed=40)
+            g = torch.Generator().manual_seed(seed)
+            pool = base.pool_pages
+            perm = torch.randperm(pool, generator=g)
+            k = base.k_cache.clone()
+            v = base.v_cache.clone()
+            k[perm] = base.k_cache[:pool]
+            v[perm] = base.v_cache[:pool]
+            tbl = base.block_table.clone()
+            real = tbl < pool
+            tbl[real] = perm[tbl[real].long()].int()
+            out = pkv.decode(base.q.cuda(), k.cuda(), v.cuda(), tbl.cuda(), base.seq_lens.cuda(),
+                             bsz, base.scale, partition_tokens=256, max_seq_len=base.max_seq_len)
+            torch.cuda.synchronize()
+            outs.append(bits(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert_bf16_close(torch.from_numpy(outs[0].view(np.int16)).view(torch.bfloat16),
+                      oracle_case(base)[0], what="invariance")
+
+
+def test_repeat_runs_bitwise_and_direct_path():
+    case = synth.build_case("rep", lens=[2000, 65, 1], block_size=832, seed=51, device="cuda")
+    a = bits(run_decode(case, 192))
+    b = bits(run_decode(case, 192))
+    assert np.array_equal(a, b)
+    ref = oracle_case(case)[0]
+    direct = run_decode(case, 2048)          # one partition: the split kernel writes out itself
+    assert pkv.plan(params_of(case, 2048))["num_partitions"] == 1
+    assert_bf16_close(direct, ref, what="direct path")
+
+
+def test_empty_sequences_give_zero_rows():
+    case = synth.build_case("empty", lens=[0, 100, 0], block_size=64, seed=52, device="cuda")
+    ref = oracle_case(case, seqs=[1])[0]
+    for ptok in (64, 4096):
+        out = run_decode(case, ptok)
+        o = f64(out)
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        assert_bf16_close(out, ref, rows=[1], what=f"empty P={ptok}")
+
+
+# ------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("name", ["long_l8192_b832", "long_l16384_b832", "long_l32768_b832"])
+def test_long_sequence_workloads(name):
+    case = synth.make_case(name, device="cuda")
+    ref, _ = oracle_case(case)
+    for ptok in (0, 512):
+        print(f"[gpu] {name} P={ptok}", flush=True)
+        assert_bf16_close(run_decode(case, ptok), ref, what=f"{name} P={ptok}")
+
+
+def test_page784_vs_page832_ab():
+    a = synth.make_case("ab_l32768_b784", device="cuda")
+    b = synth.make_case("ab_l32768_b832", device="cuda")
+    oa, ob = run_decode(a), run_decode(b)
+    assert np.array_equal(bits(oa), bits(ob)), "page784 and page832 outputs differ"
+    ref, _ = oracle_case(a)
+    assert_bf16_close(oa, ref, what="ab784")
+
+
+def test_batched_long_context_workload():
+    case = synth.make_case("batched_8seq_t131072_b832", device="cuda")
+    out = run_decode(case)
+    print(f"[gpu] batched plan {pkv.plan(params_of(case))}", flush=True)
+    assert_bf16_close(out, oracle_case(case)[0], what="batched")
+
+
+def test_wide_serving_batch_sampled():
+    case = synth.make_case("wide_64seq_b832_p4096", device="cuda")
+    assert case.partition_tokens == 4096
+    out = run_decode(case)
+    o = f64(out)
+    assert np.all(np.isfinite(o))
+    lens = np.array(case.lens)
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
+    q = f64(case.q)
+    for s in picks:
+        ref, _ = od.attention_decode(q[s], f64(case.keys(s)), f64(case.values(s)), case.scale)
+        assert_bf16_close(out[s], ref, what=f"wide s={s} L={case.lens[s]}")
+    print(f"[gpu] wide checked seqs {picks}", flush=True)
