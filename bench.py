@@ -51,8 +51,8 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measure(name, steps, warmup, torch, pkv, synth):
-    case = synth.make_case(name, device="cuda")
+def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
+    case = synth.make_case(name, device="cuda", **case_overrides)
     nbytes = case.algorithmic_bytes()
     copies = max(1, math.ceil(COLD_BYTES / nbytes))
     if copies > 1:
@@ -94,38 +94,34 @@ def measure(name, steps, warmup, torch, pkv, synth):
 
     g_step = capture(step, steps)
     g_split = capture(split_only, steps)
-    g_step.replay()             # first replay off the clock
-    g_split.replay()
-    torch.cuda.synchronize()
+    g_warm = capture(lambda i: step(0), steps)
+
+    def timed(graph):
+        """Replay on `stream`, events on the same stream; returns (wall s, gpu ms)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1)
+
+    for g in (g_step, g_split, g_warm):   # first replays off the clock
+        timed(g)
 
     # timed region: exactly `steps` steps, synchronized on both sides
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    g_step.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-
+    wall_s, gpu_ms = timed(g_step)
     # the split kernel alone, back to back, HIP events on its stream
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    g_split.replay()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    split_us = s0.elapsed_time(s1) * 1e3 / steps
-
+    _, split_ms = timed(g_split)
+    split_us = split_ms * 1e3 / steps
     # warm: the same step repeated on one copy (cache-resident where it fits)
-    g_warm = capture(lambda i: step(0), steps)
-    g_warm.replay()
-    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
-    g_warm.replay()
-    w1.record(stream)
-    torch.cuda.synchronize()
-    warm_us = w0.elapsed_time(w1) * 1e3 / steps
+    _, warm_ms = timed(g_warm)
+    warm_us = warm_ms * 1e3 / steps
+    if gpu_ms > wall_s * 1e3 * 1.01 or nbytes / (split_us * 1e-6) > 2 * PEAK_GBPS * 1e9:
+        raise RuntimeError(f"implausible timing for {name}: wall {wall_s * 1e3:.3f} ms, "
+                           f"events {gpu_ms:.3f} ms, split {split_us:.3f} us")
 
     us_step = wall_s * 1e6 / steps
     res = {
@@ -233,7 +229,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workloads", choices=["main", "all"], default="all")
+    ap.add_argument("--workloads", default="all",
+                    help="main, all, or one workload name (timed alone, reported as extra)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also launch the plain copy kernel (counter calibration runs)")
@@ -258,6 +255,12 @@ def main():
     if args.copy_probe:
         copy_probe(torch, pkv)
 
+    if args.workloads not in ("main", "all"):
+        if args.workloads not in synth.WORKLOADS:
+            sys.exit(f"unknown workload {args.workloads}; choose from {sorted(synth.WORKLOADS)}")
+        res = measure(args.workloads, args.steps, args.warmup, torch, pkv, synth)
+        print(json.dumps({"workload_only": res}), flush=True)
+        return
     main_res = measure(MAIN, args.steps, args.warmup, torch, pkv, synth)
     extra = []
     if args.workloads == "all":

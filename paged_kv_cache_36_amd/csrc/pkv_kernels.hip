@@ -1,20 +1,24 @@
 // HIP kernels for single-token decode attention over a paged KV cache, gfx950.
 //
-// Work split. One workgroup (4 waves) owns one (sequence, KV head, partition)
-// triple; a partition is a run of P consecutive tokens of the sequence. Inside
-// it, wave w takes the 16-token blocks that start at t_begin + 16 w + 64 k,
-// so the workgroup streams 64-token tiles. Each wave keeps its own running
-// softmax state for the 6 query heads of the group and the four states are
-// merged once, at the end, through LDS.
+// Work split. One workgroup (4 waves) owns one (sequence, partition, KV head)
+// triple; a partition is a run of P consecutive tokens of the sequence. The
+// grid enumerates the KV head fastest, so the workgroups that read the four
+// 512-byte head slices of the same 2 KiB token rows are dispatched together.
+// Inside a workgroup, wave w takes the 16-token blocks that start at
+// t_begin + 16 w + 64 k, so the workgroup streams 64-token tiles. Each wave
+// keeps its own running softmax state for the 6 query heads of the group and
+// the four states are merged once, at the end, through LDS.
 //
 // Per 16-token block a wave
-//  - resolves the block's page once (block sizes are multiples of 16, so a
-//    16-token block never straddles a page: one table lookup per block, no
-//    per-token division, no tail mask except on the last block of a
-//    partition),
+//  - takes the block's physical page from a per-wave list of the partition's
+//    page ids (fetched once, one id per lane, read back with v_readlane), so
+//    the block table is read once per partition and never inside the loop;
+//    block sizes are multiples of 16, so a 16-token block never straddles a
+//    page and only the last block of a partition needs a tail mask,
 //  - loads K straight into the A-operand layout of v_mfma_f32_16x16x32_bf16
 //    (lane = token (lane & 15), 16 contiguous bytes per k-step) and V as
-//    4 dims per lane (one 512-byte row per wave instruction),
+//    4 dims per lane (one 512-byte row per wave instruction), both with
+//    nontemporal loads (every byte is read once), one block ahead of use,
 //  - computes the 16 x 6 scores with 8 MFMAs against the resident q fragment,
 //  - updates (m, l) and rescales the accumulator (online softmax),
 //  - accumulates p * V in fp32 on the VALU (p is broadcast through a
@@ -47,6 +51,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kProbeBlocks = 2048;
+constexpr int kCombineWaves = 4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() {
@@ -78,103 +83,309 @@ __device__ __forceinline__ void wave_lds_sync() {
 // ---------------------------------------------------------------------------
 // Page walker: the address of a 16-token block of one sequence.
 // Token t lives in logical page t / B at offset t % B; its physical page is
-// block_table[s, t / B]. The walker keeps (logical page, offset) and moves by
-// whole blocks, so the only division is at the start of a partition.
+// block_table[s, t / B]. The walker keeps (logical page, offset), moves by
+// whole blocks (the only division is at the start of a partition) and reads
+// physical page ids from a list that lane i of the wave holds for logical
+// page `list_base + i`, fetched with one coalesced load per 64 pages.
 // ---------------------------------------------------------------------------
 struct PageWalker {
   const int32_t* row;  // block_table row of the sequence
   int32_t bsz;
   int32_t lp;          // logical page of the current block
   int32_t off;         // offset of the block's first token inside that page
+  int32_t lp_end;      // one past the last logical page the partition touches
+  int32_t list_base;   // logical page held by lane 0 of `ids`
+  int32_t ids;         // physical page id of logical page list_base + lane
 
-  __device__ __forceinline__ void init(const int32_t* r, int32_t b, int32_t t) {
+  __device__ __forceinline__ void fetch(int lane) {
+    const int32_t j = list_base + lane;
+    ids = j < lp_end ? row[j] : 0;
+  }
+  __device__ __forceinline__ void init(const int32_t* r, int32_t b, int32_t t, int32_t t_end,
+                                       int lane) {
     row = r;
     bsz = b;
     lp = t / b;
     off = t - lp * b;
+    lp_end = (t_end + b - 1) / b;
+    list_base = lp;
+    fetch(lane);
   }
-  __device__ __forceinline__ void advance(int32_t step) {
+  template <bool kRefetch>
+  __device__ __forceinline__ void advance(int32_t step, int lane) {
     off += step;
     while (off >= bsz) {
       off -= bsz;
       ++lp;
     }
+    if (kRefetch && lp - list_base >= 64) {  // pages smaller than a partition / 64
+      list_base = lp;
+      fetch(lane);
+    }
+  }
+  __device__ __forceinline__ int32_t page() const {
+    return __builtin_amdgcn_readlane(ids, lp - list_base);
   }
   // Element offset of the block's first row for one KV head.
   __device__ __forceinline__ int64_t base(int64_t page_stride, int32_t row_stride,
                                          int32_t head_off) const {
-    return static_cast<int64_t>(row[lp]) * page_stride +
-           static_cast<int64_t>(off) * row_stride + head_off;
+    return static_cast<int64_t>(page()) * page_stride + static_cast<int64_t>(off) * row_stride +
+           head_off;
   }
 };
+
+// Buffer resource over the 16 rows of a block that start at `rows` (uniform).
+// Loads through it carry a VGPR offset per lane and an SGPR offset per row, so
+// one block costs one base pointer instead of a 64-bit address per row.
+constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit data format (gfx9 family)
+// Cache policy of the block loads. A V instruction reads whole 512-byte rows
+// (full 128-byte lines) and every V byte is read once, so V streams past the
+// caches (nontemporal). A K instruction reads 64 of the 128 bytes of each of
+// 16 lines (the MFMA operand layout) and the next instruction reads the other
+// half, so K keeps the default policy and the second half hits in L2.
+constexpr int kPolicyK = 0;
+constexpr int kPolicyV = 2;                // nontemporal
+// With live == false the resource has no records: every load through it
+// returns 0 without touching memory (used for the prefetch past a wave's last
+// block, so the loop issues the same loads on every path).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* rows,
+                                                             int32_t row_bytes, bool live) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows), 0,
+                                           live ? kWaveTokens * row_bytes : 0, kBufferWord3);
+}
 
 // K block in the A-operand layout of v_mfma_f32_16x16x32_bf16: lane l holds
 // token (l & 15), and for k-step ks the 8 dims 32 ks + 8 (l >> 4) .. + 7.
-// Rows past the valid count repeat the last valid row (finite data; their
-// scores are masked to -inf).
+// All 16 rows are read even past the last valid token: a block never leaves
+// its page, so they are in-bounds page memory, and their scores are masked to
+// -inf before use. `voff` is the lane's byte offset, k_lane_offset().
 struct KBlock {
   u32x4 r[8];
 };
-__device__ __forceinline__ void load_k_block(const uint16_t* __restrict__ k, int64_t base,
-                                             int32_t row_stride, int n_valid, int lane,
-                                             KBlock& kb) {
-  const int i = min(lane & 15, n_valid - 1);
-  const uint16_t* p = k + base + static_cast<int64_t>(i) * row_stride + 8 * (lane >> 4);
+__device__ __forceinline__ int k_lane_offset(int lane, int32_t row_bytes) {
+  return (lane & 15) * row_bytes + 16 * (lane >> 4);
+}
+__device__ __forceinline__ void load_k_block(const uint16_t* rows, int32_t row_bytes, int voff,
+                                             KBlock& kb, bool live = true) {
+  const __amdgpu_buffer_rsrc_t rs = block_rsrc(rows, row_bytes, live);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) kb.r[ks] = *reinterpret_cast<const u32x4*>(p + 32 * ks);
+  for (int ks = 0; ks < 8; ++ks)
+    kb.r[ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * ks, 0, kPolicyK);
 }
 
 // V block: lane l holds dims 4 l .. 4 l + 3 of each of the 16 tokens (one
-// 512-byte row per wave instruction). Rows past the valid count repeat the
-// last valid row; their softmax weights are exactly 0.
+// 512-byte row per wave instruction). Rows after `last` (the block's last
+// valid row, 0..15) repeat row `last`: finite data whose softmax weights are
+// exactly 0 (V rows past the sequence may be NaN, and 0 * NaN is NaN).
 struct VBlock {
   u32x2 r[16];
 };
-__device__ __forceinline__ void load_v_block(const uint16_t* __restrict__ v, int64_t base,
-                                             int32_t row_stride, int n_valid, int lane,
-                                             VBlock& vb) {
-  const uint16_t* p = v + base + 4 * lane;
+__device__ __forceinline__ void load_v_block(const uint16_t* rows, int32_t row_bytes, int last,
+                                             int lane, VBlock& vb, bool live = true) {
+  const __amdgpu_buffer_rsrc_t rs = block_rsrc(rows, row_bytes, live);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int ii = min(i, n_valid - 1);
-    vb.r[i] = *reinterpret_cast<const u32x2*>(p + static_cast<int64_t>(ii) * row_stride);
+  for (int i = 0; i < kWaveTokens; ++i) {
+    const int ii = i < last ? i : last;
+    vb.r[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, ii * row_bytes, kPolicyV);
   }
 }
 
-// q of the 6 heads of KV group g in the B-operand layout: lane l holds head
-// (l & 15) (zero for heads >= 6) and, for k-step ks, dims 32 ks + 8 (l >> 4).
-__device__ __forceinline__ void load_q_frag(const uint16_t* __restrict__ q, int64_t head0,
-                                            int lane, bf16x8 (&qf)[8]) {
-  const int n = lane & 15;
-  if (n < kG) {
-    const uint16_t* p = q + (head0 + n) * kD + 8 * (lane >> 4);
+// LDS geometry (elements of 16 bits). Rows are padded so that the transposed
+// V reads (16 rows x 32 bytes per instruction) and the q fragment reads fall
+// on distinct banks.
+constexpr int kQStride = kD + 8;          // q row: 256 dims + 16 bytes pad
+constexpr int kVStride = kD + 16;         // V row: 256 dims + 32 bytes pad
+constexpr int kVWaveElems = kWaveTokens * kVStride;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Running softmax state of one wave for the 6 query heads of its group.
+// Lane l works for head n = l & 15 (lanes with n >= 6 duplicate head 5 and
+// are ignored); the output accumulator is the C layout of the 16x16 MFMA for
+// O^T[dims][heads]: acc[db][r] is dim 16 db + 4 (l >> 4) + r of head n.
+struct WaveState {
+  float m;          // running max of scale*log2(e)*score
+  float l;          // running sum of weights over this lane's tokens
+  f32x4 acc[16];
+};
+
+// fp32 -> bf16 round-to-nearest-even bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One 16-token block of one wave:
+//  scores S^T[token][head] = K . q by 8 MFMAs (16x16x32, K from registers,
+//  q fragments from LDS), online softmax update, then P.V on MFMA:
+//  O^T[dim][head] += V^T[dim][token] . P^T[token][head] with 16x16x16 MFMAs.
+//  The P^T operand is the score tile's own layout (lane: head n, tokens
+//  4j..4j+3); it is split p = p_hi + p_lo into two bf16 operands so the
+//  weights keep ~16 bits. V^T comes from the V rows staged in LDS through the
+//  transposing read ds_read_b64_tr_b16: within each 16-lane group, lane i's
+//  k-th value is element i % 4 of the 8 bytes addressed by lane i / 4 + 4 k,
+//  so lane (j, s) addresses V[4 j + s / 4][16 db + 4 (s % 4)] and receives
+//  V[4 j + k][16 db + i].
+__device__ __forceinline__ void process_block(const KBlock& kb, const VBlock& vb,
+                                              const uint16_t* lds_q, uint16_t* lds_vw, int t,
+                                              int t_end, float scale_log2, int lane,
+                                              WaveState& st) {
+  const int n = lane & 15;   // head column of the score tile
+  const int j = lane >> 4;   // row group of the score tile (tokens 4j .. 4j+3)
+
+  // stage this block's V rows (lane holds dims 4 lane .. +3 of each token)
+  // into LDS for the transposing reads below
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 32 * ks));
-  } else {
+  for (int i = 0; i < kWaveTokens; ++i)
+    *reinterpret_cast<u32x2*>(lds_vw + i * kVStride + 4 * lane) = vb.r[i];
+
+  // scores
+  const uint16_t* qrow = lds_q + min(n, kG - 1) * kQStride + 8 * j;
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.r[ks]),
+                                                __builtin_bit_cast(bf16x8, qv), sc, 0, 0, 0);
   }
+
+  // online softmax update, in log2 units
+  float sv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = sc[r] * scale_log2;
+    if (t + 4 * j + r >= t_end) sv[r] = -INFINITY;
+  }
+  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(st.m, bm);
+  float pv[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pv[r] = exp2_fast(sv[r] - m_new);
+    psum += pv[r];
+  }
+  // rescale only when some head's running max moved (alpha != 1 somewhere)
+  if (__builtin_amdgcn_ballot_w64(m_new != st.m)) {
+    const float alpha = exp2_fast(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) st.acc[db] *= alpha;
+  }
+  st.l += psum;
+  st.m = m_new;
+
+  // P^T operands: p = hi + lo, both bf16
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = bf16_rne_bits(pv[r]);
+    lo[r] = bf16_rne_bits(pv[r] - __uint_as_float(hi[r] << 16));
+  }
+  const s16x4 p_hi = __builtin_bit_cast(s16x4, u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
+  const s16x4 p_lo = __builtin_bit_cast(s16x4, u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
+
+  wave_lds_sync();   // V rows visible to the whole wave
+  const int s = lane & 15;
+  const uint16_t* vsrc = lds_vw + (4 * j + (s >> 2)) * kVStride + 4 * (s & 3);
+  s16x4 va[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+    va[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vsrc + 16 * db));
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], p_hi, st.acc[db], 0, 0, 0);
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], p_lo, st.acc[db], 0, 0, 0);
+  wave_lds_sync();   // V rows consumed before the next block overwrites them
+}
+
+// Block loads of one wave: K and V of tokens [tt, tt + 16) for the walker's
+// current block. Past t_end the loads go through an empty resource (no
+// memory traffic), so every path of the loop issues the same loads and each
+// block waits only for its own data.
+struct BlockLoader {
+  const LaunchArgs& a;
+  const PageWalker& walker;
+  int t_end, row_stride, row_bytes, head_off, voff_k, lane;
+  __device__ __forceinline__ void operator()(int tt, KBlock& kk, VBlock& vv) const {
+    const bool live = tt < t_end;
+    // last valid row of the block (select + min only: stays on the scalar unit)
+    const int n_left = live ? t_end - tt : kWaveTokens;
+    const int last = (n_left < kWaveTokens ? n_left : kWaveTokens) - 1;
+    load_k_block(a.k + walker.base(a.k_page_stride, row_stride, head_off), row_bytes, voff_k, kk,
+                 live);
+    load_v_block(a.v + walker.base(a.v_page_stride, row_stride, head_off), row_bytes, last, lane,
+                 vv, live);
+  }
+};
+
+// A wave's walk over its blocks t, t + 64, ... < t_end of one partition with
+// two register buffers for K and V used alternately: the next block is in
+// flight while the current one is consumed. The first block is already in
+// (ka, va). kRefetch selects the walker that may refetch the page list inside
+// the loop (a refetch makes the wave wait for all of its loads, so the common
+// case keeps it out of the loop entirely).
+template <bool kRefetch>
+__device__ __forceinline__ void stream_partition(const LaunchArgs& a, PageWalker& walker,
+                                                 const BlockLoader& load, KBlock& ka, VBlock& va,
+                                                 const uint16_t* lds_q, uint16_t* lds_vw, int t,
+                                                 int t_end, int lane, WaveState& st) {
+  KBlock kb;
+  VBlock vb;
+  for (;;) {
+    walker.advance<kRefetch>(kTileTokens, lane);
+    load(t + kTileTokens, kb, vb);
+    process_block(ka, va, lds_q, lds_vw, t, t_end, a.scale_log2, lane, st);
+    t += kTileTokens;
+    if (t >= t_end) break;
+    walker.advance<kRefetch>(kTileTokens, lane);
+    load(t + kTileTokens, ka, va);
+    process_block(kb, vb, lds_q, lds_vw, t, t_end, a.scale_log2, lane, st);
+    t += kTileTokens;
+    if (t >= t_end) break;
+  }
+}
+
+// Workgroup coordinates of a split-kernel launch: KV head fastest.
+struct SplitCoord {
+  int s, part, g;
+};
+__device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
+  int bid = blockIdx.x;
+  SplitCoord c;
+  c.g = bid % a.num_kv_heads;
+  bid /= a.num_kv_heads;
+  c.part = bid % a.n_parts;
+  c.s = bid / a.n_parts;
+  return c;
 }
 
 // ---------------------------------------------------------------------------
 // Split-KV partition kernel.
 // ---------------------------------------------------------------------------
-template <bool kDirect>
-__global__ __launch_bounds__(kThreads) void split_decode_kernel(LaunchArgs a) {
-  __shared__ float lds_p[kWaves][kWaveTokens][8];
-  __shared__ float lds_alpha[kWaves][8];
-  __shared__ float lds_acc[kWaves][kG][kD];
+// kRefetch: the partition may span more than 64 pages (pages smaller than
+// P / 63 tokens), so the page list is refetched inside the loop; chosen on
+// the host from P and the block size.
+template <bool kDirect, bool kRefetch>
+__global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_q[kG * kQStride];
+  // per-wave V staging rows; after the loop each wave reuses its own slice
+  // for its partial output [kG][kD] fp32
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kWaves][kVWaveElems];
   __shared__ float lds_m[kWaves][8];
   __shared__ float lds_l[kWaves][8];
+  static_assert(kVWaveElems * 2 >= kG * kD * 4, "wave slice too small for the merge");
 
   const int lane = lane_id();
   const int w = wave_id();
-  int bid = blockIdx.x;
-  const int part = bid % a.n_parts;
-  bid /= a.n_parts;
-  const int g = bid % a.num_kv_heads;
-  const int s = bid / a.num_kv_heads;
+  const SplitCoord c = split_coord(a);
+  const int s = c.s, part = c.part, g = c.g;
   const int hq = a.num_kv_heads * kG;
   const int64_t head0 = static_cast<int64_t>(s) * hq + g * kG;
   const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
@@ -194,116 +405,56 @@ __global__ __launch_bounds__(kThreads) void split_decode_kernel(LaunchArgs a) {
   const int row_stride = a.num_kv_heads * kD;
   const int head_off = g * kD;
 
-  bf16x8 qf[8];
-  load_q_frag(a.q, head0, lane, qf);
-
-  const int n = lane & 15;   // head column of the score tile
-  const int j = lane >> 4;   // row group of the score tile (tokens 4j .. 4j+3)
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float acc[kG][4];
-#pragma unroll
-  for (int h = 0; h < kG; ++h)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[h][c] = 0.f;
-
-  PageWalker walker;
+  // Start-up, ordered so the first K/V loads wait on one memory round trip:
+  // the page list and q are fetched together, the first block is issued as
+  // soon as the page list is in, and q goes to LDS while that block is in
+  // flight. Every wave issues the same loads (a wave with no block loads
+  // through an empty resource), so the waits stay exact.
+  uint16_t* lds_vw = lds_v[w];
   int t = t_begin + w * kWaveTokens;
-  KBlock kc, kn;
-  VBlock vc, vn;
-  if (t < t_end) {
-    walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t);
-    const int nv = min(kWaveTokens, t_end - t);
-    load_k_block(a.k, walker.base(a.k_page_stride, row_stride, head_off), row_stride, nv, lane, kc);
-    load_v_block(a.v, walker.base(a.v_page_stride, row_stride, head_off), row_stride, nv, lane, vc);
-  }
+  const bool active = t < t_end;
+  PageWalker walker;
+  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t, t_end,
+              lane);
+  // q: 6 rows x 512 bytes, 16 bytes per thread for threads < 192 (the others
+  // load a duplicate and do not store it)
+  const bool q_thread = threadIdx.x < kG * kD / 8;
+  const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q + (head0 + qh) * kD + 8 * qc);
+  __builtin_amdgcn_sched_barrier(0);   // keep the q load ahead of the block loads
+  const int row_bytes = row_stride * 2;
+  const BlockLoader load{a, walker, t_end, row_stride, row_bytes, head_off,
+                         k_lane_offset(lane, row_bytes), lane};
+  KBlock ka;
+  VBlock va;
+  load(t, ka, va);
+  __builtin_amdgcn_sched_barrier(0);   // issue the first block before waiting for q
+  if (q_thread) *reinterpret_cast<u32x4*>(lds_q + qh * kQStride + 8 * qc) = qv;
+  __syncthreads();
 
-  while (t < t_end) {
-    const int t_next = t + kTileTokens;
-    if (t_next < t_end) {  // prefetch the wave's next block
-      walker.advance(kTileTokens);
-      const int nvn = min(kWaveTokens, t_end - t_next);
-      load_k_block(a.k, walker.base(a.k_page_stride, row_stride, head_off), row_stride, nvn, lane,
-                   kn);
-      load_v_block(a.v, walker.base(a.v_page_stride, row_stride, head_off), row_stride, nvn, lane,
-                   vn);
-    }
-
-    // scores: S^T[token][head] = K[token][:] . q[head][:]
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  WaveState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc.r[ks]), qf[ks],
-                                                  sc, 0, 0, 0);
-
-    // online softmax update, in log2 units
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = sc[r] * a.scale_log2;
-      if (t + 4 * j + r >= t_end) sv[r] = -INFINITY;
-    }
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = exp2_fast(m_run - m_new);
-    float pv[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = exp2_fast(sv[r] - m_new);
-      psum += pv[r];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // broadcast p[token][head] and alpha[head] to the whole wave
-    if (n < kG) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lds_p[w][4 * j + r][n] = pv[r];
-      if (j == 0) lds_alpha[w][n] = alpha;
-    }
-    wave_lds_sync();
-
-    float al[kG];
-#pragma unroll
-    for (int h = 0; h < kG; ++h) al[h] = lds_alpha[w][h];
-#pragma unroll
-    for (int h = 0; h < kG; ++h)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[h][c] *= al[h];
-
-#pragma unroll
-    for (int i = 0; i < kWaveTokens; ++i) {
-      const float4 pa = *reinterpret_cast<const float4*>(&lds_p[w][i][0]);
-      const float2 pb = *reinterpret_cast<const float2*>(&lds_p[w][i][4]);
-      const float pw[kG] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y};
-      const float vf[4] = {bf16_lo(vc.r[i].x), bf16_hi(vc.r[i].x), bf16_lo(vc.r[i].y),
-                           bf16_hi(vc.r[i].y)};
-#pragma unroll
-      for (int h = 0; h < kG; ++h)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[h][c] = fmaf(pw[h], vf[c], acc[h][c]);
-    }
-    wave_lds_sync();
-
-    kc = kn;
-    vc = vn;
-    t = t_next;
-  }
+  for (int db = 0; db < 16; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (active)
+    stream_partition<kRefetch>(a, walker, load, ka, va, lds_q, lds_vw, t, t_end, lane, st);
 
   // merge the four waves' states
-  float l_tot = l_run + __shfl_xor(l_run, 16);
+  const int n = lane & 15;
+  const int j = lane >> 4;
+  float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (n < kG && j == 0) {
-    lds_m[w][n] = m_run;
-    lds_l[w][n] = l_tot;
-  }
+  float* acc_w = reinterpret_cast<float*>(lds_vw);   // this wave's slice, [kG][kD]
+  if (n < kG) {
+    if (j == 0) {
+      lds_m[w][n] = st.m;
+      lds_l[w][n] = l_tot;
+    }
 #pragma unroll
-  for (int h = 0; h < kG; ++h)
-    *reinterpret_cast<float4*>(&lds_acc[w][h][4 * lane]) =
-        make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+    for (int db = 0; db < 16; ++db)
+      *reinterpret_cast<f32x4*>(acc_w + n * kD + 16 * db + 4 * j) = st.acc[db];
+  }
   __syncthreads();
 
   const int d = threadIdx.x;
@@ -317,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void split_decode_kernel(LaunchArgs a) {
     for (int ww = 0; ww < kWaves; ++ww) {
       const float f = exp2_fast(lds_m[ww][h] - mx);
       den = fmaf(f, lds_l[ww][h], den);
-      num = fmaf(f, lds_acc[ww][h][d], num);
+      num = fmaf(f, reinterpret_cast<const float*>(lds_v[ww])[h * kD + d], num);
     }
     const float o = num / den;
     if (kDirect) {
@@ -333,82 +484,123 @@ __global__ __launch_bounds__(kThreads) void split_decode_kernel(LaunchArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp combine: one wave per (sequence, query head).
+// Log-sum-exp combine: one workgroup (4 waves) per (sequence, query head).
 // o = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M), M = max_p lse_p.
+// Wave w takes partitions w, w + 4, ...; lane l owns dims 4 l .. 4 l + 3.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void combine_kernel(LaunchArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(LaunchArgs a) {
+  __shared__ float lds_red[kCombineWaves][64];
+  __shared__ float4 lds_acc[kCombineWaves][64];
+  __shared__ float lds_den[kCombineWaves];
+
+  const int lane = lane_id();
+  const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
   const int s = blockIdx.x / hq;
   const int h = blockIdx.x - s * hq;
   const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
   const int np = (seq_len + a.partition_tokens - 1) / a.partition_tokens;
   const int64_t row = static_cast<int64_t>(s) * hq + h;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (np > 0) {
-    const float* lse = a.lse_part + row * a.n_parts;
-    float mx = -INFINITY;
-    for (int p = lane; p < np; p += 64) mx = fmaxf(mx, lse[p]);
+  const float* lse = a.lse_part + row * a.n_parts;
+
+  // M = max_p lse_p over the whole workgroup
+  float mx = -INFINITY;
+  for (int p = threadIdx.x; p < np; p += 64 * kCombineWaves) mx = fmaxf(mx, lse[p]);
 #pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-    const float* op = a.o_part + row * a.n_parts * kD + 4 * lane;
-    float den = 0.f;
-    for (int p = 0; p < np; ++p) {
-      const float wgt = exp2_fast((lse[p] - mx) * kLog2e);
-      const float4 x = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * kD);
-      den += wgt;
-      o.x = fmaf(wgt, x.x, o.x);
-      o.y = fmaf(wgt, x.y, o.y);
-      o.z = fmaf(wgt, x.z, o.z);
-      o.w = fmaf(wgt, x.w, o.w);
-    }
-    const float inv = 1.f / den;
-    o.x *= inv;
-    o.y *= inv;
-    o.z *= inv;
-    o.w *= inv;
+  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  if (lane == 0) lds_red[w][0] = mx;
+  __syncthreads();
+  mx = lds_red[0][0];
+#pragma unroll
+  for (int ww = 1; ww < kCombineWaves; ++ww) mx = fmaxf(mx, lds_red[ww][0]);
+
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  const float* op = a.o_part + row * a.n_parts * kD + 4 * lane;
+  auto add = [&](int p) {
+    const float wgt = exp2_fast((lse[p] - mx) * kLog2e);
+    const float4 x = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * kD);
+    den += wgt;
+    o.x = fmaf(wgt, x.x, o.x);
+    o.y = fmaf(wgt, x.y, o.y);
+    o.z = fmaf(wgt, x.z, o.z);
+    o.w = fmaf(wgt, x.w, o.w);
+  };
+  int p = w;
+  for (; p + 3 * kCombineWaves < np; p += 4 * kCombineWaves) {
+    add(p);
+    add(p + kCombineWaves);
+    add(p + 2 * kCombineWaves);
+    add(p + 3 * kCombineWaves);
+  }
+  for (; p < np; p += kCombineWaves) add(p);
+
+  lds_acc[w][lane] = o;
+  if (lane == 0) lds_den[w] = den;
+  __syncthreads();
+  if (w != 0) return;
+  float4 r = lds_acc[0][lane];
+  float dsum = lds_den[0];
+#pragma unroll
+  for (int ww = 1; ww < kCombineWaves; ++ww) {
+    const float4 x = lds_acc[ww][lane];
+    r.x += x.x;
+    r.y += x.y;
+    r.z += x.z;
+    r.w += x.w;
+    dsum += lds_den[ww];
+  }
+  if (np > 0) {
+    const float inv = 1.f / dsum;
+    r.x *= inv;
+    r.y *= inv;
+    r.z *= inv;
+    r.w *= inv;
   }
   const int64_t idx = row * kD + 4 * lane;
   if (a.out) {
     u32x2 packed;
-    packed.x = f32_to_bf16(o.x) | (f32_to_bf16(o.y) << 16);
-    packed.y = f32_to_bf16(o.z) | (f32_to_bf16(o.w) << 16);
+    packed.x = f32_to_bf16(r.x) | (f32_to_bf16(r.y) << 16);
+    packed.y = f32_to_bf16(r.z) | (f32_to_bf16(r.w) << 16);
     *reinterpret_cast<u32x2*>(a.out + idx) = packed;
   }
-  if (a.out_f32) *reinterpret_cast<float4*>(a.out_f32 + idx) = o;
+  if (a.out_f32) *reinterpret_cast<float4*>(a.out_f32 + idx) = r;
 }
 
 // ---------------------------------------------------------------------------
-// Debug kernels: the same partition / wave / block walk as the split kernel.
+// Debug kernels: the same workgroup coordinates, partition / wave / block walk
+// and page walker as the split kernel.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fill_i64_kernel(int64_t* p, int64_t n, int64_t value) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
     p[i] = value;
 }
 
-__global__ __launch_bounds__(kThreads) void debug_resolve_kernel(LaunchArgs a, int32_t g,
+__global__ __launch_bounds__(kThreads) void debug_resolve_kernel(LaunchArgs a, int32_t kv_head,
                                                                  int64_t* offs) {
   const int lane = lane_id();
   const int w = wave_id();
-  const int part = blockIdx.x % a.n_parts;
-  const int s = blockIdx.x / a.n_parts;
-  const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
-  const int t_begin = part * a.partition_tokens;
+  const SplitCoord c = split_coord(a);
+  if (c.g != kv_head) return;
+  const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
+  const int t_begin = c.part * a.partition_tokens;
   if (t_begin >= seq_len) return;
   const int t_end = min(t_begin + a.partition_tokens, seq_len);
   const int row_stride = a.num_kv_heads * kD;
-  PageWalker walker;
   int t = t_begin + w * kWaveTokens;
-  if (t < t_end)
-    walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t);
-  while (t < t_end) {
+  if (t >= t_end) return;
+  PageWalker walker;
+  walker.init(a.block_table + static_cast<int64_t>(c.s) * a.max_blocks, a.block_size, t, t_end,
+              lane);
+  for (;;) {
     const int nv = min(kWaveTokens, t_end - t);
-    const int64_t base = walker.base(a.k_page_stride, row_stride, g * kD);
+    const int64_t base = walker.base(a.k_page_stride, row_stride, c.g * kD);
     if (lane < nv)
-      offs[static_cast<int64_t>(s) * a.max_seq_len + t + lane] =
+      offs[static_cast<int64_t>(c.s) * a.max_seq_len + t + lane] =
           base + static_cast<int64_t>(lane) * row_stride;
     t += kTileTokens;
-    if (t < t_end) walker.advance(kTileTokens);
+    if (t >= t_end) break;
+    walker.advance<true>(kTileTokens, lane);
   }
 }
 
@@ -416,21 +608,19 @@ __global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, in
                                                                 uint16_t* dense) {
   const int lane = lane_id();
   const int w = wave_id();
-  int bid = blockIdx.x;
-  const int part = bid % a.n_parts;
-  bid /= a.n_parts;
-  const int g = bid % a.num_kv_heads;
-  const int s = bid / a.num_kv_heads;
+  const SplitCoord c = split_coord(a);
+  const int s = c.s, g = c.g;
   const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
-  const int t_begin = part * a.partition_tokens;
+  const int t_begin = c.part * a.partition_tokens;
   if (t_begin >= seq_len) return;
   const int t_end = min(t_begin + a.partition_tokens, seq_len);
   const int row_stride = a.num_kv_heads * kD;
-  PageWalker walker;
   int t = t_begin + w * kWaveTokens;
-  if (t < t_end)
-    walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t);
-  while (t < t_end) {
+  if (t >= t_end) return;
+  PageWalker walker;
+  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t, t_end,
+              lane);
+  for (;;) {
     const int nv = min(kWaveTokens, t_end - t);
     const int64_t base = walker.base(a.k_page_stride, row_stride, g * kD);
     auto dense_row = [&](int i) {
@@ -438,7 +628,7 @@ __global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, in
     };
     if (which == 0) {
       KBlock kb;
-      load_k_block(a.k, base, row_stride, nv, lane, kb);
+      load_k_block(a.k + base, row_stride * 2, k_lane_offset(lane, row_stride * 2), kb);
       const int i = lane & 15;
       if (i < nv) {
 #pragma unroll
@@ -447,13 +637,14 @@ __global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, in
       }
     } else {
       VBlock vb;
-      load_v_block(a.k, base, row_stride, nv, lane, vb);
+      load_v_block(a.k + base, row_stride * 2, nv - 1, lane, vb);
 #pragma unroll
       for (int i = 0; i < kWaveTokens; ++i)
         if (i < nv) *reinterpret_cast<u32x2*>(dense_row(i) + 4 * lane) = vb.r[i];
     }
     t += kTileTokens;
-    if (t < t_end) walker.advance(kTileTokens);
+    if (t >= t_end) break;
+    walker.advance<true>(kTileTokens, lane);
   }
 }
 
@@ -465,14 +656,16 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   uint32_t x = 0;
   int64_t i = blockIdx.x * 256ll + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a0 = buf[i], a1 = buf[i + stride], a2 = buf[i + 2 * stride], a3 = buf[i + 3 * stride];
-    x ^= (a0.x + a0.y + a0.z + a0.w) ^ (a1.x + a1.y + a1.z + a1.w) ^
-         (a2.x + a2.y + a2.z + a2.w) ^ (a3.x + a3.y + a3.z + a3.w);
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u].x + v[u].y + v[u].z + v[u].w;
   }
   for (; i < n16; i += stride) {
-    const u32x4 a0 = buf[i];
-    x ^= a0.x + a0.y + a0.z + a0.w;
+    const u32x4 v = buf[i];
+    x ^= v.x + v.y + v.z + v.w;
   }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) x ^= __shfl_xor(x, sh);
@@ -490,22 +683,27 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(u32x4* __restrict__ dst
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
+bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size) {
+  // a wave's blocks start at most 48 tokens into the partition and the walker
+  // lists 64 logical pages from its first block's page
+  return (partition_tokens + block_size - 1) / block_size + 1 > 64;
+}
+
 hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
   if (blocks == 0) return hipSuccess;
-  if (direct)
-    hipLaunchKernelGGL(split_decode_kernel<true>, dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(split_decode_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kThreads), 0, stream, a);
+  const bool refetch = partition_needs_refetch(a.partition_tokens, a.block_size);
+  auto kern = direct ? (refetch ? split_decode_kernel<true, true> : split_decode_kernel<true, false>)
+                     : (refetch ? split_decode_kernel<false, true> : split_decode_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const LaunchArgs& a, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kCombineWaves),
+                     0, stream, a);
   return hipGetLastError();
 }
 
@@ -517,7 +715,7 @@ hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* o
                      static_cast<int64_t>(-1));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.n_parts;
+  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
   hipLaunchKernelGGL(debug_resolve_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
                      stream, a, kv_head, offsets);
   return hipGetLastError();
