@@ -50,8 +50,7 @@ constexpr int kG = kGroup;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
-constexpr int kProbeBlocks = 2048;
-constexpr int kCombineWaves = 4;
+constexpr int kProbeBlocks = 16384;   // read probe: 64 workgroups per CU keep enough loads in flight
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() {
@@ -484,87 +483,91 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp combine: one workgroup (4 waves) per (sequence, query head).
-// o = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M), M = max_p lse_p.
-// Wave w takes partitions w, w + 4, ...; lane l owns dims 4 l .. 4 l + 3.
+// Log-sum-exp combine: o = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M),
+// M = max_p lse_p. One workgroup per (sequence, query head, quarter of the
+// 256 dims). Pass 1 turns the partition log-sum-exps into weights in LDS
+// (chunks of kCombineChunk partitions); pass 2 has 16 partition lanes x 16
+// dim lanes (4 dims each) with 8 independent loads in flight per thread, and
+// the 16 partition lanes are summed through LDS at the end.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(LaunchArgs a) {
-  __shared__ float lds_red[kCombineWaves][64];
-  __shared__ float4 lds_acc[kCombineWaves][64];
-  __shared__ float lds_den[kCombineWaves];
+constexpr int kCombineThreads = 256;
+constexpr int kCombineChunk = 2048;
+constexpr int kCombinePLanes = 16;
 
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) {
+  __shared__ float lds_w[kCombineChunk];
+  __shared__ float lds_red[kCombineThreads / 64];
+  __shared__ f32x4 lds_acc[kCombinePLanes][16];
+
+  const int tid = threadIdx.x;
   const int lane = lane_id();
   const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
-  const int s = blockIdx.x / hq;
-  const int h = blockIdx.x - s * hq;
+  const int quarter = blockIdx.x & 3;
+  const int row_id = blockIdx.x >> 2;
+  const int s = row_id / hq;
+  const int h = row_id - s * hq;
   const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
   const int np = (seq_len + a.partition_tokens - 1) / a.partition_tokens;
   const int64_t row = static_cast<int64_t>(s) * hq + h;
   const float* lse = a.lse_part + row * a.n_parts;
 
-  // M = max_p lse_p over the whole workgroup
+  // M = max_p lse_p
   float mx = -INFINITY;
-  for (int p = threadIdx.x; p < np; p += 64 * kCombineWaves) mx = fmaxf(mx, lse[p]);
+  for (int p = tid; p < np; p += kCombineThreads) mx = fmaxf(mx, lse[p]);
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-  if (lane == 0) lds_red[w][0] = mx;
+  if (lane == 0) lds_red[w] = mx;
   __syncthreads();
-  mx = lds_red[0][0];
-#pragma unroll
-  for (int ww = 1; ww < kCombineWaves; ++ww) mx = fmaxf(mx, lds_red[ww][0]);
+  mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
 
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int pl = tid >> 4;           // partition lane 0..15
+  const int dl = tid & 15;           // dim lane: dims 64 quarter + 4 dl .. + 3
+  const float* op = a.o_part + row * a.n_parts * kD + 64 * quarter + 4 * dl;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  const float* op = a.o_part + row * a.n_parts * kD + 4 * lane;
-  auto add = [&](int p) {
-    const float wgt = exp2_fast((lse[p] - mx) * kLog2e);
-    const float4 x = *reinterpret_cast<const float4*>(op + static_cast<int64_t>(p) * kD);
-    den += wgt;
-    o.x = fmaf(wgt, x.x, o.x);
-    o.y = fmaf(wgt, x.y, o.y);
-    o.z = fmaf(wgt, x.z, o.z);
-    o.w = fmaf(wgt, x.w, o.w);
-  };
-  int p = w;
-  for (; p + 3 * kCombineWaves < np; p += 4 * kCombineWaves) {
-    add(p);
-    add(p + kCombineWaves);
-    add(p + 2 * kCombineWaves);
-    add(p + 3 * kCombineWaves);
-  }
-  for (; p < np; p += kCombineWaves) add(p);
-
-  lds_acc[w][lane] = o;
-  if (lane == 0) lds_den[w] = den;
-  __syncthreads();
-  if (w != 0) return;
-  float4 r = lds_acc[0][lane];
-  float dsum = lds_den[0];
+  for (int c0 = 0; c0 < np; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, np - c0);
+    __syncthreads();   // previous chunk's weights consumed
+    for (int p = tid; p < cn; p += kCombineThreads) {
+      const float wgt = exp2_fast((lse[c0 + p] - mx) * kLog2e);
+      lds_w[p] = wgt;
+      den += wgt;
+    }
+    __syncthreads();
+    int p = pl;
+    for (; p + 7 * kCombinePLanes < cn; p += 8 * kCombinePLanes) {
+      f32x4 x[8];
 #pragma unroll
-  for (int ww = 1; ww < kCombineWaves; ++ww) {
-    const float4 x = lds_acc[ww][lane];
-    r.x += x.x;
-    r.y += x.y;
-    r.z += x.z;
-    r.w += x.w;
-    dsum += lds_den[ww];
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const f32x4*>(op + static_cast<int64_t>(c0 + p + u * kCombinePLanes) * kD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += lds_w[p + u * kCombinePLanes] * x[u];
+    }
+    for (; p < cn; p += kCombinePLanes)
+      acc += lds_w[p] * *reinterpret_cast<const f32x4*>(op + static_cast<int64_t>(c0 + p) * kD);
   }
-  if (np > 0) {
-    const float inv = 1.f / dsum;
-    r.x *= inv;
-    r.y *= inv;
-    r.z *= inv;
-    r.w *= inv;
-  }
-  const int64_t idx = row * kD + 4 * lane;
+  // den: sum over all threads (each partition's weight was added once)
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) den += __shfl_xor(den, sh);
+  __syncthreads();
+  if (lane == 0) lds_red[w] = den;
+  lds_acc[pl][dl] = acc;
+  __syncthreads();
+  if (tid >= 16) return;
+  den = lds_red[0] + lds_red[1] + lds_red[2] + lds_red[3];
+  f32x4 r = lds_acc[0][tid];
+#pragma unroll
+  for (int q = 1; q < kCombinePLanes; ++q) r += lds_acc[q][tid];
+  if (np > 0) r *= 1.f / den;
+  const int64_t idx = row * kD + 64 * quarter + 4 * tid;
   if (a.out) {
     u32x2 packed;
     packed.x = f32_to_bf16(r.x) | (f32_to_bf16(r.y) << 16);
     packed.y = f32_to_bf16(r.z) | (f32_to_bf16(r.w) << 16);
     *reinterpret_cast<u32x2*>(a.out + idx) = packed;
   }
-  if (a.out_f32) *reinterpret_cast<float4*>(a.out_f32 + idx) = r;
+  if (a.out_f32) *reinterpret_cast<f32x4*>(a.out_f32 + idx) = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -700,9 +703,9 @@ hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const LaunchArgs& a, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG;
+  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG * 4;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kCombineWaves),
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kCombineThreads),
                      0, stream, a);
   return hipGetLastError();
 }
