@@ -76,8 +76,15 @@ def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
                    case.scale, max_seq_len=max_len, partition_tokens=case.partition_tokens,
                    out=out, workspace=ws)
 
+    balanced = bool(plan["balanced"])
+
     def split_only(i):
-        pkv.split(prm, case.q, k_big, v_big, tables[i % copies], case.seq_lens, o_part, lse_part)
+        # the split launch pkv_decode makes for this plan, alone
+        if balanced:
+            pkv.split_balanced(prm, case.q, k_big, v_big, tables[i % copies], case.seq_lens, ws)
+        else:
+            pkv.split(prm, case.q, k_big, v_big, tables[i % copies], case.seq_lens, o_part,
+                      lse_part)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -127,7 +134,9 @@ def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
     res = {
         "workload": name, "num_seqs": case.num_seqs, "total_tokens": sum(case.lens),
         "max_seq_len": max_len, "block_size": case.block_size,
-        "partition_tokens": plan["partition_tokens"], "num_partitions": n_parts,
+        "split": "balanced" if balanced else "fixed",
+        "partition_tokens": 0 if balanced else plan["partition_tokens"],
+        "num_partitions": 0 if balanced else n_parts,
         "split_workgroups": plan["split_workgroups"], "cold_copies": copies, "steps": steps,
         "algorithmic_bytes": nbytes,
         "us_per_step": round(us_step, 3),
@@ -290,12 +299,14 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V in a NaN-poisoned shuffled page pool)",
         "config": {"workload": MAIN, "num_seqs": 1, "kv_len": 8192, "block_size": 832,
                    "q_heads": 24, "kv_heads": 4, "head_size": 256,
-                   "partition_tokens": main_res["partition_tokens"],
+                   "split": main_res["split"],
+                   "split_workgroups": main_res["split_workgroups"],
                    "cold_copies": main_res["cold_copies"]},
         "gbps": main_res["gbps_step"],
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_decode_kernel",
+            "kernel": ("balanced_split_kernel" if main_res["split"] == "balanced"
+                       else "split_decode_kernel"),
             "achieved": main_res["gbps_split"],
             "peak": PEAK_GBPS,
             "unit": "GB/s",

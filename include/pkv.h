@@ -55,7 +55,8 @@ typedef enum {
   PKV_ERR_BLOCK_SIZE = -3,  /* block_size not a positive multiple of 16           */
   PKV_ERR_PARTITION = -4,   /* partition_tokens not 0 and not a multiple of 64    */
   PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
-  PKV_ERR_UNSUPPORTED = -6, /* head_size != 256 or group size != 6                */
+  PKV_ERR_UNSUPPORTED = -6, /* head_size != 256, group size != 6, or the call does
+                               not apply to this plan                             */
   PKV_ERR_HIP = -7,         /* a HIP launch or runtime call failed                */
   PKV_ERR_STRIDE = -8       /* page stride too small or not a multiple of 8       */
 } pkv_status;
@@ -79,12 +80,21 @@ typedef struct {
   float scale;                /* softmax scale (1/sqrt(256) = 1/16 for D = 256)     */
 } pkv_decode_params;
 
-/* What a call with these params will launch (host-only query, no GPU use). */
+/* What a call with these params will launch (host-only query, no GPU use).
+ * pkv_decode with partition_tokens == 0 uses the balanced split: a fixed
+ * number of workgroups G share the batch's 64-token tiles evenly, whatever
+ * the length mix, and each (sequence, KV head) run of a workgroup's range is
+ * one partial. With an explicit partition size, and always in pkv_split /
+ * pkv_decode_partials / pkv_combine, partitions are P tokens long. */
 typedef struct {
-  int32_t partition_tokens;      /* P in use                                       */
+  int32_t partition_tokens;      /* P of the fixed partitions (pkv_split,
+                                    pkv_decode_partials; pkv_decode when P != 0) */
   int32_t num_partitions;        /* ceil(max_seq_len / P), at least 1              */
-  int32_t split_workgroups;      /* S * Hkv * num_partitions                       */
-  int32_t combine_workgroups;    /* S * Hq, or 0 when one partition covers all     */
+  int32_t split_workgroups;      /* workgroups of pkv_decode's split launch: G, or
+                                    S * Hkv * num_partitions                       */
+  int32_t combine_workgroups;    /* pkv_decode's combine launch (S * Hq * 4), or 0
+                                    when one fixed partition covers every sequence */
+  int32_t balanced;              /* 1 when pkv_decode uses the balanced split      */
   int32_t full_groups_per_page;  /* block_size / 64 (12 for 784, 13 for 832)       */
   int32_t tail_tokens_per_page;  /* block_size % 64 (16 for 784, 0 for 832)        */
   int64_t workspace_bytes;       /* what pkv_decode needs in `workspace`           */
@@ -112,16 +122,18 @@ PKV_API size_t pkv_decode_workspace_bytes(const pkv_decode_params* params);
  *   value_cache  same with v_page_stride
  *   block_table  int32 [S, max_blocks_per_seq]
  *   seq_lens     int32 [S]
- * Device output:
+ * Device outputs:
  *   out          bf16 [S, Hq, D], round-to-nearest-even from fp32
+ *   out_f32      fp32 [S, Hq, D] before the cast, or NULL
  * Workspace: device memory of at least pkv_decode_workspace_bytes(params)
  * bytes, 256-byte aligned (may be NULL when that is 0); contents on entry are
- * ignored and clobbered. Launches the split-KV partition kernel and, when more
- * than one partition is planned, the log-sum-exp combine kernel. */
+ * ignored and clobbered. Launches the split kernel (balanced or fixed
+ * partitions, see pkv_plan_info) and, unless one fixed partition covers every
+ * sequence, the log-sum-exp combine kernel. */
 PKV_API pkv_status pkv_decode(const pkv_decode_params* params, const void* q,
                       const void* key_cache, const void* value_cache,
                       const int32_t* block_table, const int32_t* seq_lens,
-                      void* out, void* workspace, size_t workspace_bytes,
+                      void* out, float* out_f32, void* workspace, size_t workspace_bytes,
                       void* stream);
 
 /* Same computation with the intermediate fp32 results exposed (for checks):
@@ -147,6 +159,21 @@ PKV_API pkv_status pkv_split(const pkv_decode_params* params, const void* q, con
                      const void* value_cache, const int32_t* block_table,
                      const int32_t* seq_lens, float* o_partial, float* lse_partial,
                      void* stream);
+
+/* The two launches of pkv_decode when partition_tokens == 0 (the balanced
+ * split, pkv_plan_info.balanced == 1), separately: pkv_split_balanced writes
+ * the partials and tile prefix sums into `workspace` (at least
+ * pkv_decode_workspace_bytes(params) bytes, 256-byte aligned; the layout is
+ * internal), and pkv_combine_balanced turns that workspace into out (bf16,
+ * may be NULL) and out_f32 (fp32, may be NULL). Returns PKV_ERR_UNSUPPORTED
+ * when these params do not select the balanced split. */
+PKV_API pkv_status pkv_split_balanced(const pkv_decode_params* params, const void* q,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* workspace, size_t workspace_bytes, void* stream);
+PKV_API pkv_status pkv_combine_balanced(const pkv_decode_params* params, const int32_t* seq_lens,
+                                const void* workspace, size_t workspace_bytes, void* out,
+                                float* out_f32, void* stream);
 
 /* The log-sum-exp combine on its own: merges partitions of size P (from
  * pkv_plan(params)) laid out as in pkv_decode_partials into out (bf16,

@@ -9,6 +9,7 @@ from ._lib import LIB_PATH, LibraryMissing, load  # noqa: F401
 from .api import (  # noqa: F401
     PkvError,
     combine,
+    combine_balanced,
     debug_gather,
     debug_resolve,
     decode,
@@ -18,5 +19,6 @@ from .api import (  # noqa: F401
     probe_copy,
     probe_read,
     split,
+    split_balanced,
     workspace_bytes,
 )

@@ -39,6 +39,7 @@ class PlanInfo(ctypes.Structure):
         ("num_partitions", ctypes.c_int32),
         ("split_workgroups", ctypes.c_int32),
         ("combine_workgroups", ctypes.c_int32),
+        ("balanced", ctypes.c_int32),
         ("full_groups_per_page", ctypes.c_int32),
         ("tail_tokens_per_page", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
@@ -56,10 +57,12 @@ SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_plan": (_I32, [_P, ctypes.POINTER(PlanInfo)]),
     "pkv_decode_workspace_bytes": (_SZ, [_P]),
-    "pkv_decode": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "pkv_decode": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "pkv_decode_partials": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_split": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_combine": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_split_balanced": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "pkv_combine_balanced": (_I32, [_P, _VP, _VP, _SZ, _VP, _VP, _VP]),
     "pkv_debug_resolve": (_I32, [_P, _I32, _VP, _VP, _VP, _VP]),
     "pkv_debug_gather": (_I32, [_P, _I32, _VP, _VP, _VP, _VP, _VP]),
     "pkv_probe_sink_floats": (_I32, []),

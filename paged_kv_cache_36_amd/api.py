@@ -114,11 +114,13 @@ def _seq_lens(seq_lens, s):
 
 
 def decode(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, *,
-           max_seq_len=None, partition_tokens=0, out=None, workspace=None, stream=None):
+           max_seq_len=None, partition_tokens=0, out=None, out_f32=None, workspace=None,
+           stream=None):
     """o = softmax(q K^T * scale) V per sequence, K/V read through block_table.
 
     Returns ``out`` (bf16 [S, Hq, D]); allocates it (and the workspace) with
-    torch when not given.
+    torch when not given. ``out_f32`` (fp32 [S, Hq, D]), when given, also
+    receives the result before the bf16 cast.
     """
     p = make_params(q, key_cache, value_cache, block_table, block_size, scale,
                     max_seq_len, partition_tokens)
@@ -130,8 +132,8 @@ def decode(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().pkv_decode(ctypes.byref(p), _ptr(q), _ptr(key_cache), _ptr(value_cache),
-                             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(workspace),
-                             ws_bytes, _stream(stream)), "pkv_decode")
+                             _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(out_f32),
+                             _ptr(workspace), ws_bytes, _stream(stream)), "pkv_decode")
     return out
 
 
@@ -160,6 +162,24 @@ def split(params: DecodeParams, q, key_cache, value_cache, block_table, seq_lens
     _check(load().pkv_split(ctypes.byref(params), _ptr(q), _ptr(key_cache), _ptr(value_cache),
                             _ptr(block_table), _ptr(seq_lens), _ptr(o_partial),
                             _ptr(lse_partial), _stream(stream)), "pkv_split")
+
+
+def split_balanced(params: DecodeParams, q, key_cache, value_cache, block_table, seq_lens,
+                   workspace, stream=None):
+    """First half of decode() with the balanced split: partials into workspace."""
+    _check(load().pkv_split_balanced(ctypes.byref(params), _ptr(q), _ptr(key_cache),
+                                     _ptr(value_cache), _ptr(block_table), _ptr(seq_lens),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)), "pkv_split_balanced")
+
+
+def combine_balanced(params: DecodeParams, seq_lens, workspace, *, out=None, out_f32=None,
+                     stream=None):
+    """Second half of decode() with the balanced split."""
+    _check(load().pkv_combine_balanced(ctypes.byref(params), _ptr(seq_lens), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(out),
+                                       _ptr(out_f32), _stream(stream)), "pkv_combine_balanced")
+    return out, out_f32
 
 
 def combine(params: DecodeParams, o_partial, lse_partial, seq_lens, *, out=None, out_f32=None,

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -35,10 +36,18 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Balanced split (pkv_decode with partition_tokens == 0): G workgroups, about
+// 1-2 per CU of a 256-CU gfx950 part, never more than the tiles there can be.
+constexpr int64_t kPlanCUs = 256;
+
 struct Plan {
-  int32_t P = 0;
-  int32_t n_parts = 0;
+  bool balanced = false;
+  int32_t P = 0;            // fixed partitions: tokens per partition
+  int32_t n_parts = 0;      // fixed partitions: ceil(max_seq_len / P)
+  int32_t grid = 0;         // balanced: workgroups G
+  bool refetch = false;     // a segment may span more than the walker's 64 page ids
   size_t o_part_bytes = 0;
+  size_t lse_bytes = 0;
   size_t workspace = 0;
 };
 
@@ -64,7 +73,9 @@ pkv_status check_params(const pkv_decode_params* p) {
   return PKV_OK;
 }
 
-Plan make_plan(const pkv_decode_params* p) {
+// Fixed partitions (pkv_split, pkv_decode_partials, and pkv_decode with an
+// explicit partition size).
+Plan make_fixed_plan(const pkv_decode_params* p) {
   Plan pl;
   int32_t P = p->partition_tokens;
   if (P == 0) {
@@ -80,11 +91,43 @@ Plan make_plan(const pkv_decode_params* p) {
   }
   pl.P = P;
   pl.n_parts = p->max_seq_len > 0 ? (p->max_seq_len + P - 1) / P : 1;
+  pl.refetch = pkv::partition_needs_refetch(P, p->block_size);
   if (pl.n_parts > 1) {
     const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * pl.n_parts;
     pl.o_part_bytes = round_up(rows * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
-    pl.workspace = pl.o_part_bytes + round_up(rows * sizeof(float), kWorkspaceAlign);
+    pl.lse_bytes = round_up(rows * sizeof(float), kWorkspaceAlign);
+    pl.workspace = pl.o_part_bytes + pl.lse_bytes;
   }
+  return pl;
+}
+
+// The plan pkv_decode runs: the balanced split when the partition size is
+// left to the library (and the batch fits its limits), fixed partitions
+// otherwise.
+Plan make_decode_plan(const pkv_decode_params* p) {
+  const int64_t tiles_per_seq = (static_cast<int64_t>(p->max_seq_len) + pkv::kTileTokens - 1) /
+                                pkv::kTileTokens;
+  const int64_t t_max = static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * tiles_per_seq;
+  if (p->partition_tokens != 0 || p->num_seqs > pkv::kMaxBalancedSeqs || t_max < 1 ||
+      t_max > (int64_t{1} << 30))
+    return make_fixed_plan(p);
+  Plan pl;
+  pl.balanced = true;
+  int64_t g = t_max / 8;             // at least ~8 tiles per workgroup when work allows
+  if (g < kPlanCUs) g = kPlanCUs;
+  if (g > 2 * kPlanCUs) g = 2 * kPlanCUs;
+  if (g > t_max) g = t_max;
+  pl.grid = static_cast<int32_t>(g);
+  // longest run of one (sequence, KV head) a workgroup can get
+  const int64_t seg_tokens = std::min<int64_t>(
+      p->max_seq_len, ((t_max + g - 1) / g + 1) * pkv::kTileTokens);
+  pl.refetch = pkv::partition_needs_refetch(static_cast<int32_t>((seg_tokens + 63) / 64 * 64),
+                                            p->block_size);
+  const size_t slots = static_cast<size_t>(g) + static_cast<size_t>(p->num_seqs) * p->num_kv_heads;
+  pl.o_part_bytes = round_up(slots * pkv::kGroup * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
+  pl.lse_bytes = round_up(slots * pkv::kGroup * sizeof(float), kWorkspaceAlign);
+  pl.workspace = pl.o_part_bytes + pl.lse_bytes +
+                 round_up((static_cast<size_t>(p->num_seqs) + 1) * sizeof(int32_t), kWorkspaceAlign);
   return pl;
 }
 
@@ -100,19 +143,26 @@ pkv::LaunchArgs base_args(const pkv_decode_params* p, const Plan& pl) {
   a.partition_tokens = pl.P;
   a.n_parts = pl.n_parts;
   a.max_seq_len = p->max_seq_len;
+  a.balanced_grid = pl.balanced ? pl.grid : 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
   return a;
+}
+
+int64_t split_workgroups(const pkv_decode_params* p, const Plan& pl) {
+  return pl.balanced ? pl.grid : static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * pl.n_parts;
 }
 
 void log_plan(const char* what, const pkv_decode_params* p, const Plan& pl) {
   if (!log_enabled()) return;
   std::fprintf(stderr,
                "[pkv] %s: S=%d Hq=%d Hkv=%d D=%d block_size=%d (64-token groups %d, tail %d) "
-               "max_seq_len=%d P=%d partitions=%d split_wg=%lld combine=%s workspace=%zu\n",
+               "max_seq_len=%d %s P=%d partitions=%d split_wg=%lld refetch=%d combine=%s "
+               "workspace=%zu\n",
                what, p->num_seqs, p->num_q_heads, p->num_kv_heads, p->head_size, p->block_size,
-               p->block_size / 64, p->block_size % 64, p->max_seq_len, pl.P, pl.n_parts,
-               static_cast<long long>(p->num_seqs) * p->num_kv_heads * pl.n_parts,
-               pl.n_parts > 1 ? "yes" : "no", pl.workspace);
+               p->block_size / 64, p->block_size % 64, p->max_seq_len,
+               pl.balanced ? "balanced" : "fixed", pl.P, pl.n_parts,
+               static_cast<long long>(split_workgroups(p, pl)), pl.refetch ? 1 : 0,
+               (pl.balanced || pl.n_parts > 1) ? "yes" : "no", pl.workspace);
 }
 
 pkv_status check_inputs(const void* q, const void* k, const void* v, const int32_t* bt,
@@ -124,6 +174,21 @@ pkv_status check_inputs(const void* q, const void* k, const void* v, const int32
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+pkv_status check_workspace(const Plan& pl, const void* workspace, size_t workspace_bytes) {
+  if (pl.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < pl.workspace || !aligned(workspace, kWorkspaceAlign)))
+    return PKV_ERR_WORKSPACE;
+  return PKV_OK;
+}
+
+// Partials (and, for the balanced split, tile prefix sums) inside the workspace.
+void carve_workspace(const Plan& pl, void* workspace, pkv::LaunchArgs& a) {
+  char* ws = static_cast<char*>(workspace);
+  a.o_part = reinterpret_cast<float*>(ws);
+  a.lse_part = reinterpret_cast<float*>(ws + pl.o_part_bytes);
+  if (pl.balanced) a.prefix = reinterpret_cast<int32_t*>(ws + pl.o_part_bytes + pl.lse_bytes);
+}
 
 }  // namespace
 
@@ -150,36 +215,39 @@ pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info) {
   pkv_status st = check_params(params);
   if (st != PKV_OK) return st;
   if (info == nullptr) return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
-  info->partition_tokens = pl.P;
-  info->num_partitions = pl.n_parts;
-  info->split_workgroups = params->num_seqs * params->num_kv_heads * pl.n_parts;
-  info->combine_workgroups = pl.n_parts > 1 ? params->num_seqs * params->num_q_heads : 0;
+  const Plan fx = make_fixed_plan(params);
+  const Plan dec = make_decode_plan(params);
+  info->partition_tokens = fx.P;
+  info->num_partitions = fx.n_parts;
+  info->split_workgroups = static_cast<int32_t>(split_workgroups(params, dec));
+  info->combine_workgroups =
+      (dec.balanced || dec.n_parts > 1) ? params->num_seqs * params->num_q_heads * 4 : 0;
+  info->balanced = dec.balanced ? 1 : 0;
   info->full_groups_per_page = params->block_size / 64;
   info->tail_tokens_per_page = params->block_size % 64;
-  info->workspace_bytes = static_cast<int64_t>(pl.workspace);
+  info->workspace_bytes = static_cast<int64_t>(dec.workspace);
   return PKV_OK;
 }
 
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* params) {
   if (check_params(params) != PKV_OK) return 0;
-  return make_plan(params).workspace;
+  return make_decode_plan(params).workspace;
 }
 
 pkv_status pkv_decode(const pkv_decode_params* params, const void* q, const void* key_cache,
                       const void* value_cache, const int32_t* block_table,
-                      const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      const int32_t* seq_lens, void* out, float* out_f32, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   pkv_status st = check_params(params);
   if (st != PKV_OK) return st;
   if (params->num_seqs == 0) return PKV_OK;
   st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
   if (st != PKV_OK) return st;
-  if (!out || !aligned(out, 16)) return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
-  if (pl.workspace > 0 &&
-      (workspace == nullptr || workspace_bytes < pl.workspace || !aligned(workspace, kWorkspaceAlign)))
-    return PKV_ERR_WORKSPACE;
+  if (!out || !aligned(out, 16) || (out_f32 != nullptr && !aligned(out_f32, 16)))
+    return PKV_ERR_NULL;
+  const Plan pl = make_decode_plan(params);
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
   log_plan("decode", params, pl);
 
   pkv::LaunchArgs a = base_args(params, pl);
@@ -189,13 +257,57 @@ pkv_status pkv_decode(const pkv_decode_params* params, const void* q, const void
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pl.n_parts == 1) return hip_status(pkv::launch_split(a, /*direct=*/true, s));
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.o_part_bytes);
-  st = hip_status(pkv::launch_split(a, /*direct=*/false, s));
+  if (!pl.balanced && pl.n_parts == 1) return hip_status(pkv::launch_split(a, /*direct=*/true, s));
+  carve_workspace(pl, workspace, a);
+  st = pl.balanced ? hip_status(pkv::launch_balanced_split(a, pl.refetch, s))
+                   : hip_status(pkv::launch_split(a, /*direct=*/false, s));
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_combine(a, s));
+  return hip_status(pkv::launch_combine(a, pl.balanced, s));
+}
+
+pkv_status pkv_split_balanced(const pkv_decode_params* params, const void* q,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  const Plan pl = make_decode_plan(params);
+  if (!pl.balanced) return params->num_seqs == 0 ? PKV_OK : PKV_ERR_UNSUPPORTED;
+  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
+  if (st != PKV_OK) return st;
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  log_plan("split_balanced", params, pl);
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  carve_workspace(pl, workspace, a);
+  return hip_status(pkv::launch_balanced_split(a, pl.refetch, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_combine_balanced(const pkv_decode_params* params, const int32_t* seq_lens,
+                                const void* workspace, size_t workspace_bytes, void* out,
+                                float* out_f32, void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  const Plan pl = make_decode_plan(params);
+  if (!pl.balanced) return params->num_seqs == 0 ? PKV_OK : PKV_ERR_UNSUPPORTED;
+  if (!seq_lens || !aligned(seq_lens, 4) || (out != nullptr && !aligned(out, 16)) ||
+      (out_f32 != nullptr && !aligned(out_f32, 16)))
+    return PKV_ERR_NULL;
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
+  carve_workspace(pl, const_cast<void*>(workspace), a);
+  return hip_status(pkv::launch_combine(a, /*balanced=*/true, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
@@ -211,7 +323,7 @@ pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
   if (!o_partial || !lse_partial || !out_f32 || !aligned(o_partial, 16) || !aligned(out_f32, 16) ||
       (out != nullptr && !aligned(out, 16)))
     return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
+  const Plan pl = make_fixed_plan(params);
   log_plan("decode_partials", params, pl);
   pkv::LaunchArgs a = base_args(params, pl);
   a.q = static_cast<const uint16_t*>(q);
@@ -226,7 +338,7 @@ pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(pkv::launch_split(a, /*direct=*/false, s));
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_combine(a, s));
+  return hip_status(pkv::launch_combine(a, /*balanced=*/false, s));
 }
 
 pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void* key_cache,
@@ -240,7 +352,7 @@ pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void*
   if (st != PKV_OK) return st;
   if (!o_partial || !lse_partial || !aligned(o_partial, 16) || !aligned(lse_partial, 4))
     return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
+  const Plan pl = make_fixed_plan(params);
   log_plan("split", params, pl);
   pkv::LaunchArgs a = base_args(params, pl);
   a.q = static_cast<const uint16_t*>(q);
@@ -262,14 +374,14 @@ pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,
   if (!o_partial || !lse_partial || !seq_lens || !aligned(o_partial, 16) ||
       (out != nullptr && !aligned(out, 16)) || (out_f32 != nullptr && !aligned(out_f32, 16)))
     return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
+  const Plan pl = make_fixed_plan(params);
   pkv::LaunchArgs a = base_args(params, pl);
   a.seq_lens = seq_lens;
   a.o_part = const_cast<float*>(o_partial);
   a.lse_part = const_cast<float*>(lse_partial);
   a.out = static_cast<uint16_t*>(out);
   a.out_f32 = out_f32;
-  return hip_status(pkv::launch_combine(a, static_cast<hipStream_t>(stream)));
+  return hip_status(pkv::launch_combine(a, /*balanced=*/false, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
@@ -280,7 +392,7 @@ pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
   if (kv_head < 0 || kv_head >= params->num_kv_heads) return PKV_ERR_SHAPE;
   if (params->num_seqs == 0) return PKV_OK;
   if (!block_table || !seq_lens || !row_offsets || !aligned(row_offsets, 8)) return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
+  const Plan pl = make_fixed_plan(params);
   pkv::LaunchArgs a = base_args(params, pl);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
@@ -297,7 +409,7 @@ pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which, cons
   if (params->num_seqs == 0) return PKV_OK;
   if (!cache || !block_table || !seq_lens || !dense || !aligned(cache, 16) || !aligned(dense, 16))
     return PKV_ERR_NULL;
-  const Plan pl = make_plan(params);
+  const Plan pl = make_fixed_plan(params);
   pkv::LaunchArgs a = base_args(params, pl);
   a.k = static_cast<const uint16_t*>(cache);
   a.block_table = block_table;

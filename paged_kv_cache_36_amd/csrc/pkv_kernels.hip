@@ -351,7 +351,7 @@ __device__ __forceinline__ void stream_partition(const LaunchArgs& a, PageWalker
   }
 }
 
-// Workgroup coordinates of a split-kernel launch: KV head fastest.
+// Workgroup coordinates of a fixed-partition launch: KV head fastest.
 struct SplitCoord {
   int s, part, g;
 };
@@ -365,42 +365,36 @@ __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
   return c;
 }
 
-// ---------------------------------------------------------------------------
-// Split-KV partition kernel.
-// ---------------------------------------------------------------------------
-// kRefetch: the partition may span more than 64 pages (pages smaller than
-// P / 63 tokens), so the page list is refetched inside the loop; chosen on
-// the host from P and the block size.
-template <bool kDirect, bool kRefetch>
-__global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_q[kG * kQStride];
+// LDS of one split workgroup.
+struct SplitLds {
+  uint16_t q[kG * kQStride];
   // per-wave V staging rows; after the loop each wave reuses its own slice
   // for its partial output [kG][kD] fp32
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kWaves][kVWaveElems];
-  __shared__ float lds_m[kWaves][8];
-  __shared__ float lds_l[kWaves][8];
-  static_assert(kVWaveElems * 2 >= kG * kD * 4, "wave slice too small for the merge");
+  uint16_t v[kWaves][kVWaveElems];
+  float m[kWaves][8];
+  float l[kWaves][8];
+};
+static_assert(kVWaveElems * 2 >= kG * kD * 4, "wave slice too small for the merge");
 
+// Where a segment's result goes.
+enum SegmentTarget : int {
+  kToOutput = 0,       // final bf16 (+ fp32) output: the segment is the whole sequence
+  kToPartition = 1,    // o_part[s, h, part, :], lse_part[s, h, part]
+  kToSlot = 2,         // o_part[slot, h % 6, :], lse_part[slot, h % 6] (balanced split)
+};
+
+// One workgroup's pass over tokens [t_begin, t_end) of sequence s for KV
+// head g: the 4 waves stream their blocks, their states are merged through
+// LDS and the merged (o, lse) of the 6 query heads is written to `target`.
+// Ends with a workgroup barrier so the LDS can be reused right away.
+template <bool kRefetch>
+__device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, int s, int g,
+                                            int t_begin, int t_end, SegmentTarget target,
+                                            int64_t index) {
   const int lane = lane_id();
   const int w = wave_id();
-  const SplitCoord c = split_coord(a);
-  const int s = c.s, part = c.part, g = c.g;
   const int hq = a.num_kv_heads * kG;
   const int64_t head0 = static_cast<int64_t>(s) * hq + g * kG;
-  const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
-  const int t_begin = part * a.partition_tokens;
-
-  if (t_begin >= seq_len) {
-    if (kDirect && part == 0) {  // empty sequence: zero output rows
-      for (int e = threadIdx.x; e < kG * kD; e += kThreads) {
-        const int64_t o = head0 * kD + e;
-        if (a.out) a.out[o] = 0;
-        if (a.out_f32) a.out_f32[o] = 0.f;
-      }
-    }
-    return;
-  }
-  const int t_end = min(t_begin + a.partition_tokens, seq_len);
   const int row_stride = a.num_kv_heads * kD;
   const int head_off = g * kD;
 
@@ -409,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   // soon as the page list is in, and q goes to LDS while that block is in
   // flight. Every wave issues the same loads (a wave with no block loads
   // through an empty resource), so the waits stay exact.
-  uint16_t* lds_vw = lds_v[w];
+  uint16_t* lds_vw = lds.v[w];
   int t = t_begin + w * kWaveTokens;
   const bool active = t < t_end;
   PageWalker walker;
@@ -428,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   VBlock va;
   load(t, ka, va);
   __builtin_amdgcn_sched_barrier(0);   // issue the first block before waiting for q
-  if (q_thread) *reinterpret_cast<u32x4*>(lds_q + qh * kQStride + 8 * qc) = qv;
+  if (q_thread) *reinterpret_cast<u32x4*>(lds.q + qh * kQStride + 8 * qc) = qv;
   __syncthreads();
 
   WaveState st;
@@ -437,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
 #pragma unroll
   for (int db = 0; db < 16; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (active)
-    stream_partition<kRefetch>(a, walker, load, ka, va, lds_q, lds_vw, t, t_end, lane, st);
+    stream_partition<kRefetch>(a, walker, load, ka, va, lds.q, lds_vw, t, t_end, lane, st);
 
   // merge the four waves' states
   const int n = lane & 15;
@@ -447,8 +441,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   float* acc_w = reinterpret_cast<float*>(lds_vw);   // this wave's slice, [kG][kD]
   if (n < kG) {
     if (j == 0) {
-      lds_m[w][n] = st.m;
-      lds_l[w][n] = l_tot;
+      lds.m[w][n] = st.m;
+      lds.l[w][n] = l_tot;
     }
 #pragma unroll
     for (int db = 0; db < 16; ++db)
@@ -459,26 +453,138 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   const int d = threadIdx.x;
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
-    float mx = lds_m[0][h];
+    float mx = lds.m[0][h];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, lds_m[ww][h]);
+    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, lds.m[ww][h]);
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2_fast(lds_m[ww][h] - mx);
-      den = fmaf(f, lds_l[ww][h], den);
-      num = fmaf(f, reinterpret_cast<const float*>(lds_v[ww])[h * kD + d], num);
+      const float f = exp2_fast(lds.m[ww][h] - mx);
+      den = fmaf(f, lds.l[ww][h], den);
+      num = fmaf(f, reinterpret_cast<const float*>(lds.v[ww])[h * kD + d], num);
     }
     const float o = num / den;
-    if (kDirect) {
+    const float lse = (mx + __log2f(den)) * kLn2;
+    if (target == kToOutput) {
       const int64_t idx = (head0 + h) * kD + d;
       if (a.out) a.out[idx] = static_cast<uint16_t>(f32_to_bf16(o));
       if (a.out_f32) a.out_f32[idx] = o;
     } else {
-      const int64_t prow = (head0 + h) * a.n_parts + part;
+      const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index
+                                                  : index * kG + h;
       a.o_part[prow * kD + d] = o;
-      if (d == 0) a.lse_part[prow] = (mx + __log2f(den)) * kLn2;
+      if (d == 0) a.lse_part[prow] = lse;
     }
+  }
+  __syncthreads();   // LDS free for the next segment
+}
+
+// Zero output rows of the 6 query heads of (s, g): an empty sequence.
+__device__ __forceinline__ void zero_rows(const LaunchArgs& a, int s, int g) {
+  const int64_t head0 = static_cast<int64_t>(s) * a.num_kv_heads * kG + g * kG;
+  for (int e = threadIdx.x; e < kG * kD; e += kThreads) {
+    const int64_t o = head0 * kD + e;
+    if (a.out) a.out[o] = 0;
+    if (a.out_f32) a.out_f32[o] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-KV partition kernel, fixed partitions of P tokens: one workgroup per
+// (sequence, partition, KV head).
+// kRefetch: the partition may span more than 64 pages (pages smaller than
+// P / 63 tokens), so the page list is refetched inside the loop; chosen on
+// the host from P and the block size.
+// ---------------------------------------------------------------------------
+template <bool kDirect, bool kRefetch>
+__global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
+  __shared__ __attribute__((aligned(16))) SplitLds lds;
+  const SplitCoord c = split_coord(a);
+  const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
+  const int t_begin = c.part * a.partition_tokens;
+  if (t_begin >= seq_len) {
+    if (kDirect && c.part == 0) zero_rows(a, c.s, c.g);   // empty sequence
+    return;
+  }
+  const int t_end = min(t_begin + a.partition_tokens, seq_len);
+  run_segment<kRefetch>(a, lds, c.s, c.g, t_begin, t_end, kDirect ? kToOutput : kToPartition,
+                        c.part);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split-KV kernel: the work is cut into 64-token tiles, enumerated
+// as (sequence, KV head, tile), and workgroup w of G = min(grid, T) takes
+// the tiles [ceil(w T / G), ceil((w + 1) T / G)) of the T in total, so every
+// workgroup streams the same number of tiles whatever the length mix; tile u
+// belongs to workgroup floor(u G / T). A workgroup
+// writes one partial for each (sequence, KV head) run its range touches, at
+// slot w + (s * Hkv + g): along the range boundaries the pair (w, s*Hkv + g)
+// moves monotonically, so these slots are distinct. Tile prefix sums are
+// computed by every workgroup from seq_lens; workgroup 0 also stores them for
+// the combine kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tiles_of(int seq_len) {
+  return (seq_len + kTileTokens - 1) / kTileTokens;
+}
+
+template <bool kRefetch>
+__global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs a) {
+  __shared__ __attribute__((aligned(16))) SplitLds lds;
+  __shared__ int32_t pref[kMaxBalancedSeqs + 1];   // units before sequence s (x Hkv)
+  const int S = a.num_seqs;
+  const int hkv = a.num_kv_heads;
+
+  // prefix sums of Hkv * tiles, by wave 0 in chunks of 64 sequences
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    if (lane == 0) pref[0] = 0;
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int si = c0 + lane;
+      int v = si < S ? hkv * tiles_of(min(max(a.seq_lens[si], 0), a.max_seq_len)) : 0;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const int up = __shfl_up(v, sh);
+        if (lane >= sh) v += up;
+      }
+      if (si < S) pref[si + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= S; i += kThreads) a.prefix[i] = pref[i];
+
+  // G_eff = min(G, T) workgroups take part, so every range is non-empty and
+  // the owners floor(u G_eff / T) of consecutive tiles step by 0 or 1.
+  const int64_t T = pref[S];
+  const int64_t G = min(static_cast<int64_t>(gridDim.x), T);
+  const int64_t wg = blockIdx.x;
+  if (wg >= G) return;
+  const int64_t u0 = (wg * T + G - 1) / G;
+  const int64_t u1 = ((wg + 1) * T + G - 1) / G;
+
+  // sequence holding unit u0: the last s with pref[s] <= u0 (uniform search)
+  int lo = 0, hi = S;   // pref[lo] <= u0 < pref[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid] <= u0) lo = mid; else hi = mid;
+  }
+  int s = lo;
+  int64_t u = u0;
+  while (u < u1) {
+    while (u >= pref[s + 1]) ++s;   // skip sequences with no tiles
+    const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
+    const int n = tiles_of(seq_len);
+    const int64_t base = pref[s];
+    const int g = static_cast<int>((u - base) / n);
+    const int tile = static_cast<int>((u - base) - static_cast<int64_t>(g) * n);
+    const int64_t seg_end = min(u1, base + static_cast<int64_t>(g + 1) * n);
+    const int t_begin = tile * kTileTokens;
+    const int t_end = min(static_cast<int>(tile + (seg_end - u)) * kTileTokens, seq_len);
+    run_segment<kRefetch>(a, lds, s, g, t_begin, t_end, kToSlot,
+                          wg + static_cast<int64_t>(s) * hkv + g);
+    u = seg_end;
   }
 }
 
@@ -494,6 +600,7 @@ constexpr int kCombineThreads = 256;
 constexpr int kCombineChunk = 2048;
 constexpr int kCombinePLanes = 16;
 
+template <bool kBalanced>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) {
   __shared__ float lds_w[kCombineChunk];
   __shared__ float lds_red[kCombineThreads / 64];
@@ -508,44 +615,98 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
   const int s = row_id / hq;
   const int h = row_id - s * hq;
   const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
-  const int np = (seq_len + a.partition_tokens - 1) / a.partition_tokens;
   const int64_t row = static_cast<int64_t>(s) * hq + h;
-  const float* lse = a.lse_part + row * a.n_parts;
 
-  // M = max_p lse_p
-  float mx = -INFINITY;
-  for (int p = tid; p < np; p += kCombineThreads) mx = fmaxf(mx, lse[p]);
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-  if (lane == 0) lds_red[w] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
+  // The np partials of this row: partial k at o_part[o_base + k * o_stride]
+  // and lse_part[l_base + k * l_stride].
+  int np;
+  int64_t o_base, o_stride, l_base, l_stride;
+  if (kBalanced) {
+    const int g = h / kG;
+    const int n = tiles_of(seq_len);
+    const int64_t T = a.prefix[a.num_seqs];
+    const int64_t G = min(static_cast<int64_t>(a.balanced_grid), T);   // as in the split
+    const int64_t u_lo = static_cast<int64_t>(a.prefix[s]) + static_cast<int64_t>(g) * n;
+    const int64_t w_first = n > 0 ? u_lo * G / T : 0;
+    const int64_t w_last = n > 0 ? (u_lo + n - 1) * G / T : -1;
+    np = static_cast<int>(w_last - w_first + 1);
+    const int64_t slot0 = w_first + static_cast<int64_t>(s) * a.num_kv_heads + g;
+    o_base = (slot0 * kG + (h - g * kG)) * kD;
+    o_stride = kG * kD;
+    l_base = slot0 * kG + (h - g * kG);
+    l_stride = kG;
+  } else {
+    np = (seq_len + a.partition_tokens - 1) / a.partition_tokens;
+    o_base = row * a.n_parts * kD;
+    o_stride = kD;
+    l_base = row * a.n_parts;
+    l_stride = 1;
+  }
+  const float* lse = a.lse_part + l_base;
 
   const int pl = tid >> 4;           // partition lane 0..15
   const int dl = tid & 15;           // dim lane: dims 64 quarter + 4 dl .. + 3
-  const float* op = a.o_part + row * a.n_parts * kD + 64 * quarter + 4 * dl;
+  const float* op = a.o_part + o_base + 64 * quarter + 4 * dl;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int c0 = 0; c0 < np; c0 += kCombineChunk) {
-    const int cn = min(kCombineChunk, np - c0);
-    __syncthreads();   // previous chunk's weights consumed
-    for (int p = tid; p < cn; p += kCombineThreads) {
-      const float wgt = exp2_fast((lse[c0 + p] - mx) * kLog2e);
-      lds_w[p] = wgt;
-      den += wgt;
+
+  if (np <= 8 * kCombinePLanes) {
+    // One pass: every partition's partial and log-sum-exp are loaded at once
+    // (8 per thread), then M, the weights and the sums follow.
+    f32x4 x[8];
+    float ls[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = pl + u * kCombinePLanes;
+      const bool ok = p < np;
+      x[u] = ok ? *reinterpret_cast<const f32x4*>(op + p * o_stride)
+                : f32x4{0.f, 0.f, 0.f, 0.f};
+      ls[u] = ok ? lse[p * l_stride] : -INFINITY;
     }
+    float mx = ls[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) mx = fmaxf(mx, ls[u]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));   // the 4 partition lanes of this wave
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lane == 0) lds_red[w] = mx;
     __syncthreads();
-    int p = pl;
-    for (; p + 7 * kCombinePLanes < cn; p += 8 * kCombinePLanes) {
-      f32x4 x[8];
+    mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        x[u] = *reinterpret_cast<const f32x4*>(op + static_cast<int64_t>(c0 + p + u * kCombinePLanes) * kD);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += lds_w[p + u * kCombinePLanes] * x[u];
+    for (int u = 0; u < 8; ++u) {
+      const float wgt = (pl + u * kCombinePLanes < np) ? exp2_fast((ls[u] - mx) * kLog2e) : 0.f;
+      acc += wgt * x[u];
+      if (dl == 0) den += wgt;   // one dim lane per partition lane counts the weight
     }
-    for (; p < cn; p += kCombinePLanes)
-      acc += lds_w[p] * *reinterpret_cast<const f32x4*>(op + static_cast<int64_t>(c0 + p) * kD);
+  } else {
+    // Long partition lists: M first, then chunks of weights through LDS.
+    float mx = -INFINITY;
+    for (int p = tid; p < np; p += kCombineThreads) mx = fmaxf(mx, lse[p * l_stride]);
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+    if (lane == 0) lds_red[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
+    for (int c0 = 0; c0 < np; c0 += kCombineChunk) {
+      const int cn = min(kCombineChunk, np - c0);
+      __syncthreads();   // previous chunk's weights consumed
+      for (int p = tid; p < cn; p += kCombineThreads) {
+        const float wgt = exp2_fast((lse[(c0 + p) * l_stride] - mx) * kLog2e);
+        lds_w[p] = wgt;
+        den += wgt;
+      }
+      __syncthreads();
+      int p = pl;
+      for (; p + 7 * kCombinePLanes < cn; p += 8 * kCombinePLanes) {
+        f32x4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          x[u] = *reinterpret_cast<const f32x4*>(op + (c0 + p + u * kCombinePLanes) * o_stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += lds_w[p + u * kCombinePLanes] * x[u];
+      }
+      for (; p < cn; p += kCombinePLanes)
+        acc += lds_w[p] * *reinterpret_cast<const f32x4*>(op + (c0 + p) * o_stride);
+    }
   }
   // den: sum over all threads (each partition's weight was added once)
 #pragma unroll
@@ -702,11 +863,19 @@ hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const LaunchArgs& a, hipStream_t stream) {
+hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, hipStream_t stream) {
+  if (a.num_seqs == 0 || a.balanced_grid == 0) return hipSuccess;
+  auto kern = refetch ? balanced_split_kernel<true> : balanced_split_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(a.balanced_grid)), dim3(kThreads), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG * 4;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kCombineThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL(balanced ? combine_kernel<true> : combine_kernel<false>,
+                     dim3(static_cast<uint32_t>(blocks)), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ constexpr int kGroup = 6;        // query heads per KV head
 constexpr int kWaveTokens = 16;  // tokens one wave handles per step (MFMA rows)
 constexpr int kWaves = 4;        // waves per split workgroup
 constexpr int kTileTokens = kWaveTokens * kWaves;  // 64 tokens per workgroup step
+constexpr int kMaxBalancedSeqs = 4096;             // sequences the balanced split handles
 
 // Everything a split/combine/debug launch needs, already validated.
 struct LaunchArgs {
@@ -22,8 +23,9 @@ struct LaunchArgs {
   const int32_t* seq_lens;
   uint16_t* out;        // bf16 [S, Hq, D] or null
   float* out_f32;       // fp32 [S, Hq, D] or null
-  float* o_part;        // fp32 [S, Hq, n_parts, D] or null
-  float* lse_part;      // fp32 [S, Hq, n_parts] or null
+  float* o_part;        // fp32 [S, Hq, n_parts, D] (fixed P) or [slots, 6, D] (balanced)
+  float* lse_part;      // fp32 [S, Hq, n_parts] (fixed P) or [slots, 6] (balanced)
+  int32_t* prefix;      // balanced: [S + 1] tile prefix sums (x Hkv), written by the split
   int64_t k_page_stride;
   int64_t v_page_stride;
   int32_t num_seqs;
@@ -33,13 +35,17 @@ struct LaunchArgs {
   int32_t partition_tokens;
   int32_t n_parts;
   int32_t max_seq_len;
+  int32_t balanced_grid;  // balanced split: workgroups G (0 = fixed partitions)
   float scale_log2;     // scale * log2(e)
 };
 
 // split kernel: per (sequence, KV head, partition). direct=true writes the
 // final bf16 (and optional fp32) output, valid only when n_parts == 1.
 hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream);
-hipError_t launch_combine(const LaunchArgs& a, hipStream_t stream);
+// balanced split: G = a.balanced_grid workgroups share the tiles evenly.
+hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, hipStream_t stream);
+hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream);
+bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size);
 hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* offsets,
                                 hipStream_t stream);
 hipError_t launch_debug_gather(const LaunchArgs& a, int32_t which, uint16_t* dense,

@@ -83,26 +83,46 @@ def test_decode_validates_before_any_launch(lib):
     p = params()
     null = None
     fake = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
-    assert lib.pkv_decode(None, fake, fake, fake, fake, fake, fake, None, 0, None) == -1
-    assert lib.pkv_decode(ctypes.byref(p), null, fake, fake, fake, fake, fake, None, 0, None) == -1
+    dec = lib.pkv_decode
+    assert dec(None, fake, fake, fake, fake, fake, fake, None, None, 0, None) == -1
+    assert dec(ctypes.byref(p), null, fake, fake, fake, fake, fake, None, None, 0, None) == -1
     mis = ctypes.c_void_p(0x10008)    # not 16-byte aligned
-    assert lib.pkv_decode(ctypes.byref(p), mis, fake, fake, fake, fake, fake, None, 0, None) == -1
+    assert dec(ctypes.byref(p), mis, fake, fake, fake, fake, fake, None, None, 0, None) == -1
+    assert dec(ctypes.byref(p), fake, fake, fake, fake, fake, fake, mis, None, 0, None) == -1
     # multi-partition plan without a workspace
-    assert lib.pkv_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, 0, None) == -5
+    assert dec(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, 0, None) == -5
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(p))
     assert need > 0
-    assert lib.pkv_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, need - 1,
-                          None) == -5
+    assert dec(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, need - 1,
+               None) == -5
     bad = params(block_size=100)
-    assert lib.pkv_decode(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, need,
-                          None) == -3
+    assert dec(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, fake, need,
+               None) == -3
     # zero sequences is a no-op
-    assert lib.pkv_decode(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None,
-                          None, 0, None) == 0
+    assert dec(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None, None,
+               None, 0, None) == 0
     assert lib.pkv_debug_resolve(ctypes.byref(p), 4, fake, fake, fake, None) == -2
     assert lib.pkv_debug_gather(ctypes.byref(p), 2, fake, fake, fake, fake, None) == -2
     assert lib.pkv_probe_read(fake, 17, fake, None) == -1
     assert lib.pkv_probe_copy(fake, mis, 32, None) == -1
+
+
+def test_balanced_halves_validate_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x10000)
+    p = params()
+    need = lib.pkv_decode_workspace_bytes(ctypes.byref(p))
+    sb, cb = lib.pkv_split_balanced, lib.pkv_combine_balanced
+    # a fixed partition size does not select the balanced split
+    fixed = params(partition_tokens=4096)
+    assert sb(ctypes.byref(fixed), fake, fake, fake, fake, fake, fake, need, None) == -6
+    assert cb(ctypes.byref(fixed), fake, fake, need, fake, None, None) == -6
+    assert sb(ctypes.byref(p), fake, fake, fake, fake, fake, fake, need - 1, None) == -5
+    assert sb(ctypes.byref(p), fake, fake, fake, fake, fake, None, need, None) == -5
+    assert sb(ctypes.byref(p), None, fake, fake, fake, fake, fake, need, None) == -1
+    assert cb(ctypes.byref(p), None, fake, need, fake, None, None) == -1
+    assert cb(ctypes.byref(p), fake, fake, need - 1, fake, None, None) == -5
+    assert cb(ctypes.byref(params(block_size=100)), fake, fake, need, fake, None, None) == -3
+    assert sb(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None, 0, None) == 0
 
 
 def test_plan_page_geometry_matches_pages(lib):
@@ -124,21 +144,31 @@ def test_capacity_overhead_matches_pages():
 
 def test_plan_partitions_and_workspace(lib):
     st, info = plan(lib, partition_tokens=4096, max_seq_len=8192)
-    assert st == 0
+    assert st == 0 and info.balanced == 0
     assert info.partition_tokens == 4096 and info.num_partitions == 2
-    assert info.split_workgroups == 1 * 4 * 2 and info.combine_workgroups == 24
+    assert info.split_workgroups == 1 * 4 * 2 and info.combine_workgroups == 24 * 4
     rows = 1 * 24 * 2
     assert info.workspace_bytes >= rows * 256 * 4 + rows * 4
     # one partition: no combine, no workspace
     st, info = plan(lib, partition_tokens=8192, max_seq_len=8192)
     assert st == 0 and info.num_partitions == 1 and info.combine_workgroups == 0
     assert info.workspace_bytes == 0
-    # auto partition is a multiple of 64 within [64, 4096]
+    # auto: pkv_decode balances; the fixed partition size reported for
+    # pkv_split / pkv_decode_partials is a multiple of 64 within [64, 4096]
     for s, L in ((1, 8192), (8, 40000), (64, 65536), (1, 1)):
         st, info = plan(lib, num_seqs=s, max_seq_len=L, max_blocks_per_seq=(L + 831) // 832)
         assert st == 0
         assert info.partition_tokens % 64 == 0 and 64 <= info.partition_tokens <= 4096
         assert info.num_partitions == -(-L // info.partition_tokens)
+        assert info.balanced == 1
+        t_max = s * 4 * (-(-L // 64))
+        assert 1 <= info.split_workgroups <= min(512, t_max)
+        slots = info.split_workgroups + s * 4
+        assert info.workspace_bytes >= slots * 6 * 257 * 4 + (s + 1) * 4
+        assert info.combine_workgroups == s * 24 * 4
+    # too many sequences for the balanced split: fixed partitions
+    st, info = plan(lib, num_seqs=5000, max_seq_len=1024, max_blocks_per_seq=2)
+    assert st == 0 and info.balanced == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

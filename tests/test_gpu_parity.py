@@ -241,3 +241,87 @@ def test_wide_serving_batch_sampled():
         ref, _ = od.attention_decode(q[s], f64(case.keys(s)), f64(case.values(s)), case.scale)
         assert_bf16_close(out[s], ref, what=f"wide s={s} L={case.lens[s]}")
     print(f"[gpu] wide checked seqs {picks}", flush=True)
+
+
+# ------------------------------------------------------------ balanced split
+
+def run_balanced(case, max_seq_len=None):
+    """pkv_decode with the partition size left to the library (balanced)."""
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device=case.q.device)
+    out = pkv.decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                     case.block_size, case.scale, partition_tokens=0,
+                     max_seq_len=max_seq_len or max(case.max_seq_len, 1), out_f32=out32)
+    torch.cuda.synchronize()
+    return out, out32
+
+
+@pytest.mark.parametrize("lens,bsz", [
+    ([3000, 1234, 64, 65, 1], 832),
+    ([2000, 1, 1, 1], 64),          # far fewer tiles than planned workgroups
+    ([5000, 0, 777, 0], 784),       # empty sequences inside the batch
+])
+def test_balanced_split_fp32_and_bf16(lens, bsz):
+    case = synth.build_case("bal", lens=lens, block_size=bsz, seed=61, device="cuda")
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    out, out32 = run_balanced(case)
+    ref, _ = oracle_case(case)
+    got32 = f64(out32)
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got32[s] == 0) and np.all(f64(out)[s] == 0)
+        else:
+            assert_rows_rel(got32[s], ref[s], what=f"balanced fp32 s={s}")
+    assert_bf16_close(out, ref, rows=[s for s, n in enumerate(lens) if n > 0],
+                      what=f"balanced {lens}")
+
+
+def test_balanced_split_many_sequences():
+    rng = np.random.default_rng(62)
+    lens = [int(x) for x in rng.integers(1, 700, size=300)]
+    case = synth.build_case("bal300", lens=lens, block_size=832, seed=62, device="cuda")
+    out, out32 = run_balanced(case)
+    ref, _ = oracle_case(case)
+    assert_rows_rel(f64(out32), ref, what="balanced 300 seqs fp32")
+    assert_bf16_close(out, ref, what="balanced 300 seqs")
+
+
+def test_balanced_split_page_list_refetch():
+    # 16-token pages and long sequences: a workgroup's run spans more than 64
+    # pages, so the walker refetches its page list inside the loop
+    case = synth.build_case("balrf", lens=[150000, 150000], block_size=16, seed=63, device="cuda")
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    out, out32 = run_balanced(case)
+    ref, _ = oracle_case(case)
+    assert_rows_rel(f64(out32), ref, what="balanced refetch fp32")
+    assert_bf16_close(out, ref, what="balanced refetch")
+
+
+def test_balanced_split_page_size_invariant_bitwise():
+    outs = []
+    for bsz in (64, 784, 832):
+        case = synth.build_case("balinv", lens=[3000, 1234, 700], block_size=bsz, seed=64,
+                                device="cuda")
+        out, _ = run_balanced(case, max_seq_len=3000)
+        outs.append(bits(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_balanced_split_and_combine_entry_points_match_decode():
+    # the two halves of pkv_decode, called on their own, give its exact bits
+    case = synth.build_case("balhalves", lens=[3000, 1234, 64], block_size=832, seed=65,
+                            device="cuda")
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    out, out32 = run_balanced(case)
+    ws = torch.empty(pkv.workspace_bytes(prm), dtype=torch.uint8, device="cuda")
+    pkv.split_balanced(prm, case.q, case.k_cache, case.v_cache, case.block_table,
+                       case.seq_lens, ws)
+    o2 = torch.empty_like(case.q)
+    o2_32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    pkv.combine_balanced(prm, case.seq_lens, ws, out=o2, out_f32=o2_32)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o2), bits(out))
+    assert torch.equal(o2_32, out32)
