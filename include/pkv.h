@@ -74,18 +74,22 @@ typedef struct {
                                  B*Hkv*D for a [pages,B,Hkv,D] tensor, 2*B*Hkv*D
                                  for the unbind(1) view of [pages,2,B,Hkv,D]        */
   int64_t v_page_stride;      /* same for the V cache                               */
-  int32_t max_seq_len;        /* host-known upper bound on seq_lens (grid planning) */
+  int32_t max_seq_len;        /* host-known upper bound on seq_lens (grid planning;
+                                 with one sequence the partitions are sized from
+                                 it, so a tight bound keeps every CU busy)          */
   int32_t partition_tokens;   /* split-KV partition P: 0 = choose automatically,
                                  else a multiple of 64                              */
   float scale;                /* softmax scale (1/sqrt(256) = 1/16 for D = 256)     */
 } pkv_decode_params;
 
 /* What a call with these params will launch (host-only query, no GPU use).
- * pkv_decode with partition_tokens == 0 uses the balanced split: a fixed
- * number of workgroups G share the batch's 64-token tiles evenly, whatever
- * the length mix, and each (sequence, KV head) run of a workgroup's range is
- * one partial. With an explicit partition size, and always in pkv_split /
- * pkv_decode_partials / pkv_combine, partitions are P tokens long. */
+ * pkv_decode with partition_tokens == 0 and more than one sequence uses the
+ * balanced split: a fixed number of workgroups G share the batch's 64-token
+ * tiles evenly, whatever the length mix, and each (sequence, KV head) run of
+ * a workgroup's range is one partial. A single sequence (which fixed
+ * partitions already split evenly), an explicit partition size, batches of
+ * more than 4096 sequences, and pkv_split / pkv_decode_partials /
+ * pkv_combine always, use partitions of P tokens. */
 typedef struct {
   int32_t partition_tokens;      /* P of the fixed partitions (pkv_split,
                                     pkv_decode_partials; pkv_decode when P != 0) */
@@ -160,8 +164,8 @@ PKV_API pkv_status pkv_split(const pkv_decode_params* params, const void* q, con
                      const int32_t* seq_lens, float* o_partial, float* lse_partial,
                      void* stream);
 
-/* The two launches of pkv_decode when partition_tokens == 0 (the balanced
- * split, pkv_plan_info.balanced == 1), separately: pkv_split_balanced writes
+/* The two launches of pkv_decode when it uses the balanced split
+ * (pkv_plan_info.balanced == 1), separately: pkv_split_balanced writes
  * the partials and tile prefix sums into `workspace` (at least
  * pkv_decode_workspace_bytes(params) bytes, 256-byte aligned; the layout is
  * internal), and pkv_combine_balanced turns that workspace into out (bf16,

@@ -102,20 +102,24 @@ Plan make_fixed_plan(const pkv_decode_params* p) {
 }
 
 // The plan pkv_decode runs: the balanced split when the partition size is
-// left to the library (and the batch fits its limits), fixed partitions
-// otherwise.
+// left to the library and the batch has several sequences (within the
+// balanced kernel's limits); fixed partitions otherwise. One sequence is
+// split evenly by fixed partitions already, and they start one memory round
+// trip sooner (no prefix sums over the lengths before the page list).
 Plan make_decode_plan(const pkv_decode_params* p) {
   const int64_t tiles_per_seq = (static_cast<int64_t>(p->max_seq_len) + pkv::kTileTokens - 1) /
                                 pkv::kTileTokens;
   const int64_t t_max = static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * tiles_per_seq;
-  if (p->partition_tokens != 0 || p->num_seqs > pkv::kMaxBalancedSeqs || t_max < 1 ||
+  if (p->partition_tokens != 0 || p->num_seqs == 1 || p->num_seqs > pkv::kMaxBalancedSeqs ||
+      t_max < 1 ||
       t_max > (int64_t{1} << 30))
     return make_fixed_plan(p);
   Plan pl;
   pl.balanced = true;
-  int64_t g = t_max / 8;             // at least ~8 tiles per workgroup when work allows
-  if (g < kPlanCUs) g = kPlanCUs;
-  if (g > 2 * kPlanCUs) g = 2 * kPlanCUs;
+  // One workgroup per CU: each already keeps all of its first two blocks per
+  // wave in flight, and a second workgroup per CU measured slower at every
+  // batch size tried (more partials, no more bandwidth).
+  int64_t g = kPlanCUs;
   if (g > t_max) g = t_max;
   pl.grid = static_cast<int32_t>(g);
   // longest run of one (sequence, KV head) a workgroup can get

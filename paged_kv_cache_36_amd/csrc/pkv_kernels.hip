@@ -100,13 +100,15 @@ struct PageWalker {
     const int32_t j = list_base + lane;
     ids = j < lp_end ? row[j] : 0;
   }
-  __device__ __forceinline__ void init(const int32_t* r, int32_t b, int32_t t, int32_t t_end,
+  // `page_end` bounds the logical pages read from the row (one past the last);
+  // it only has to cover the blocks that are loaded and stay within the row.
+  __device__ __forceinline__ void init(const int32_t* r, int32_t b, int32_t t, int32_t page_end,
                                        int lane) {
     row = r;
     bsz = b;
     lp = t / b;
     off = t - lp * b;
-    lp_end = (t_end + b - 1) / b;
+    lp_end = page_end;
     list_base = lp;
     fetch(lane);
   }
@@ -126,6 +128,9 @@ struct PageWalker {
     return __builtin_amdgcn_readlane(ids, lp - list_base);
   }
   // Element offset of the block's first row for one KV head.
+  static __device__ __forceinline__ int32_t pages_for(int32_t t_end, int32_t b) {
+    return (t_end + b - 1) / b;
+  }
   __device__ __forceinline__ int64_t base(int64_t page_stride, int32_t row_stride,
                                          int32_t head_off) const {
     return static_cast<int64_t>(page()) * page_stride + static_cast<int64_t>(off) * row_stride +
@@ -172,20 +177,24 @@ __device__ __forceinline__ void load_k_block(const uint16_t* rows, int32_t row_b
     kb.r[ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * ks, 0, kPolicyK);
 }
 
-// V block: lane l holds dims 4 l .. 4 l + 3 of each of the 16 tokens (one
-// 512-byte row per wave instruction). Rows after `last` (the block's last
-// valid row, 0..15) repeat row `last`: finite data whose softmax weights are
-// exactly 0 (V rows past the sequence may be NaN, and 0 * NaN is NaN).
+// V block: two 512-byte rows per wave instruction (16 bytes per lane, the
+// widest load, so the block costs 8 instructions): r[i] of lane l holds dims
+// 8 (l & 31) .. + 7 of row v_row(i, l) = 2 i + (l >> 5). Rows after `last`
+// (the block's last valid row, 0..15) repeat row `last`: finite data whose
+// softmax weights are exactly 0 (V rows past the sequence may be NaN, and
+// 0 * NaN is NaN).
 struct VBlock {
-  u32x2 r[16];
+  u32x4 r[8];
 };
+__device__ __forceinline__ int v_row(int i, int lane) { return 2 * i + (lane >> 5); }
 __device__ __forceinline__ void load_v_block(const uint16_t* rows, int32_t row_bytes, int last,
                                              int lane, VBlock& vb, bool live = true) {
   const __amdgpu_buffer_rsrc_t rs = block_rsrc(rows, row_bytes, live);
 #pragma unroll
-  for (int i = 0; i < kWaveTokens; ++i) {
-    const int ii = i < last ? i : last;
-    vb.r[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, ii * row_bytes, kPolicyV);
+  for (int i = 0; i < kWaveTokens / 2; ++i) {
+    const int rr = min(v_row(i, lane), last);
+    vb.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, rr * row_bytes + 16 * (lane & 31), 0,
+                                                    kPolicyV);
   }
 }
 
@@ -236,8 +245,8 @@ __device__ __forceinline__ void process_block(const KBlock& kb, const VBlock& vb
   // stage this block's V rows (lane holds dims 4 lane .. +3 of each token)
   // into LDS for the transposing reads below
 #pragma unroll
-  for (int i = 0; i < kWaveTokens; ++i)
-    *reinterpret_cast<u32x2*>(lds_vw + i * kVStride + 4 * lane) = vb.r[i];
+  for (int i = 0; i < kWaveTokens / 2; ++i)
+    *reinterpret_cast<u32x4*>(lds_vw + v_row(i, lane) * kVStride + 8 * (lane & 31)) = vb.r[i];
 
   // scores
   const uint16_t* qrow = lds_q + min(n, kG - 1) * kQStride + 8 * j;
@@ -371,8 +380,8 @@ struct SplitLds {
   // per-wave V staging rows; after the loop each wave reuses its own slice
   // for its partial output [kG][kD] fp32
   uint16_t v[kWaves][kVWaveElems];
-  float m[kWaves][8];
-  float l[kWaves][8];
+  alignas(16) float m[kWaves][8];
+  alignas(16) float l[kWaves][8];
 };
 static_assert(kVWaveElems * 2 >= kG * kD * 4, "wave slice too small for the merge");
 
@@ -387,10 +396,30 @@ enum SegmentTarget : int {
 // head g: the 4 waves stream their blocks, their states are merged through
 // LDS and the merged (o, lse) of the 6 query heads is written to `target`.
 // Ends with a workgroup barrier so the LDS can be reused right away.
+// The loads a segment starts with: the wave's page list and its 16 bytes of q.
+// They depend on the segment's first token and a bound on its pages only, so
+// the fixed-partition kernel issues them before its sequence length arrives.
+struct SegmentStart {
+  PageWalker walker;
+  u32x4 qv;
+};
+__device__ __forceinline__ SegmentStart begin_segment(const LaunchArgs& a, int s, int g,
+                                                      int t_begin, int32_t page_end) {
+  SegmentStart su;
+  su.walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size,
+                 t_begin + wave_id() * kWaveTokens, page_end, lane_id());
+  // q: 6 rows x 512 bytes, 16 bytes per thread for threads < 192 (the others
+  // load a duplicate and do not store it)
+  const int64_t head0 = static_cast<int64_t>(s) * a.num_kv_heads * kG + g * kG;
+  const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
+  su.qv = *reinterpret_cast<const u32x4*>(a.q + (head0 + qh) * kD + 8 * qc);
+  return su;
+}
+
 template <bool kRefetch>
-__device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, int s, int g,
-                                            int t_begin, int t_end, SegmentTarget target,
-                                            int64_t index) {
+__device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, SegmentStart& su,
+                                            int s, int g, int t_begin, int t_end,
+                                            SegmentTarget target, int64_t index) {
   const int lane = lane_id();
   const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
@@ -399,21 +428,16 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   const int head_off = g * kD;
 
   // Start-up, ordered so the first K/V loads wait on one memory round trip:
-  // the page list and q are fetched together, the first block is issued as
-  // soon as the page list is in, and q goes to LDS while that block is in
-  // flight. Every wave issues the same loads (a wave with no block loads
-  // through an empty resource), so the waits stay exact.
+  // the page list and q were fetched together (begin_segment), the first
+  // block is issued as soon as the page list is in, and q goes to LDS while
+  // that block is in flight. Every wave issues the same loads (a wave with no
+  // block loads through an empty resource), so the waits stay exact.
   uint16_t* lds_vw = lds.v[w];
   int t = t_begin + w * kWaveTokens;
   const bool active = t < t_end;
-  PageWalker walker;
-  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t, t_end,
-              lane);
-  // q: 6 rows x 512 bytes, 16 bytes per thread for threads < 192 (the others
-  // load a duplicate and do not store it)
+  PageWalker& walker = su.walker;
   const bool q_thread = threadIdx.x < kG * kD / 8;
   const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
-  const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q + (head0 + qh) * kD + 8 * qc);
   __builtin_amdgcn_sched_barrier(0);   // keep the q load ahead of the block loads
   const int row_bytes = row_stride * 2;
   const BlockLoader load{a, walker, t_end, row_stride, row_bytes, head_off,
@@ -422,7 +446,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   VBlock va;
   load(t, ka, va);
   __builtin_amdgcn_sched_barrier(0);   // issue the first block before waiting for q
-  if (q_thread) *reinterpret_cast<u32x4*>(lds.q + qh * kQStride + 8 * qc) = qv;
+  if (q_thread) *reinterpret_cast<u32x4*>(lds.q + qh * kQStride + 8 * qc) = su.qv;
   __syncthreads();
 
   WaveState st;
@@ -450,20 +474,44 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   }
   __syncthreads();
 
+  // Every LDS value the merge needs is read first (the running maxima and
+  // sums of all waves as broadcast reads, and this thread's dim of each
+  // wave's partial), so the reads pay one latency instead of a chain of them.
   const int d = threadIdx.x;
+  f32x4 mv[kWaves][2], lv[kWaves][2];
+  float xv[kG][kWaves];
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    mv[ww][0] = *reinterpret_cast<const f32x4*>(&lds.m[ww][0]);
+    mv[ww][1] = *reinterpret_cast<const f32x4*>(&lds.m[ww][4]);
+    lv[ww][0] = *reinterpret_cast<const f32x4*>(&lds.l[ww][0]);
+    lv[ww][1] = *reinterpret_cast<const f32x4*>(&lds.l[ww][4]);
+  }
+#pragma unroll
+  for (int h = 0; h < kG; ++h)
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+      xv[h][ww] = reinterpret_cast<const float*>(lds.v[ww])[h * kD + d];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
-    float mx = lds.m[0][h];
+    float mw[kWaves], lw[kWaves];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, lds.m[ww][h]);
+    for (int ww = 0; ww < kWaves; ++ww) {
+      mw[ww] = mv[ww][h >> 2][h & 3];
+      lw[ww] = lv[ww][h >> 2][h & 3];
+    }
+    float mx = mw[0];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, mw[ww]);
     float den = 0.f, num = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2_fast(lds.m[ww][h] - mx);
-      den = fmaf(f, lds.l[ww][h], den);
-      num = fmaf(f, reinterpret_cast<const float*>(lds.v[ww])[h * kD + d], num);
+      const float f = exp2_fast(mw[ww] - mx);   // 0 for a wave without tokens
+      den = fmaf(f, lw[ww], den);
+      num = fmaf(f, xv[h][ww], num);
     }
-    const float o = num / den;
+    // den >= 1: the wave holding the maximum contributes its own weight 1
+    const float o = num * __builtin_amdgcn_rcpf(den);
     const float lse = (mx + __log2f(den)) * kLn2;
     if (target == kToOutput) {
       const int64_t idx = (head0 + h) * kD + d;
@@ -500,15 +548,19 @@ template <bool kDirect, bool kRefetch>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) SplitLds lds;
   const SplitCoord c = split_coord(a);
-  const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
   const int t_begin = c.part * a.partition_tokens;
+  // the partition's pages as far as max_seq_len reaches (host-checked to fit
+  // the table row), so the page list needs no sequence length
+  const int t_cap = min(t_begin + a.partition_tokens, a.max_seq_len);
+  SegmentStart su = begin_segment(a, c.s, c.g, t_begin, PageWalker::pages_for(t_cap, a.block_size));
+  const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
   if (t_begin >= seq_len) {
     if (kDirect && c.part == 0) zero_rows(a, c.s, c.g);   // empty sequence
     return;
   }
-  const int t_end = min(t_begin + a.partition_tokens, seq_len);
-  run_segment<kRefetch>(a, lds, c.s, c.g, t_begin, t_end, kDirect ? kToOutput : kToPartition,
-                        c.part);
+  const int t_end = min(t_cap, seq_len);
+  run_segment<kRefetch>(a, lds, su, c.s, c.g, t_begin, t_end,
+                        kDirect ? kToOutput : kToPartition, c.part);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,7 +634,8 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
     const int64_t seg_end = min(u1, base + static_cast<int64_t>(g + 1) * n);
     const int t_begin = tile * kTileTokens;
     const int t_end = min(static_cast<int>(tile + (seg_end - u)) * kTileTokens, seq_len);
-    run_segment<kRefetch>(a, lds, s, g, t_begin, t_end, kToSlot,
+    SegmentStart su = begin_segment(a, s, g, t_begin, PageWalker::pages_for(t_end, a.block_size));
+    run_segment<kRefetch>(a, lds, su, s, g, t_begin, t_end, kToSlot,
                           wg + static_cast<int64_t>(s) * hkv + g);
     u = seg_end;
   }
@@ -614,35 +667,58 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
   const int row_id = blockIdx.x >> 2;
   const int s = row_id / hq;
   const int h = row_id - s * hq;
-  const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
   const int64_t row = static_cast<int64_t>(s) * hq + h;
 
   // The np partials of this row: partial k at o_part[o_base + k * o_stride]
-  // and lse_part[l_base + k * l_stride].
-  int np;
+  // and lse_part[l_base + k * l_stride]. Loads are issued for k < np_load
+  // (>= np) and the partials k >= np are dropped by selects afterwards: with
+  // fixed partitions np_load = n_parts is known at launch, so the loads do
+  // not wait for the sequence length.
+  int np_load;
+  int np_balanced = 0;   // balanced: the count, known before any partial load
+  int len_v = 0;         // fixed: the raw length, in a VGPR
   int64_t o_base, o_stride, l_base, l_stride;
   if (kBalanced) {
     const int g = h / kG;
+    const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
     const int n = tiles_of(seq_len);
     const int64_t T = a.prefix[a.num_seqs];
     const int64_t G = min(static_cast<int64_t>(a.balanced_grid), T);   // as in the split
     const int64_t u_lo = static_cast<int64_t>(a.prefix[s]) + static_cast<int64_t>(g) * n;
     const int64_t w_first = n > 0 ? u_lo * G / T : 0;
     const int64_t w_last = n > 0 ? (u_lo + n - 1) * G / T : -1;
-    np = static_cast<int>(w_last - w_first + 1);
+    np_balanced = static_cast<int>(w_last - w_first + 1);
     const int64_t slot0 = w_first + static_cast<int64_t>(s) * a.num_kv_heads + g;
     o_base = (slot0 * kG + (h - g * kG)) * kD;
     o_stride = kG * kD;
     l_base = slot0 * kG + (h - g * kG);
     l_stride = kG;
+    np_load = np_balanced;
   } else {
-    np = (seq_len + a.partition_tokens - 1) / a.partition_tokens;
+    // The length goes through the vector memory path and stays in a VGPR
+    // until the selects: a scalar load would be waited for together with the
+    // kernel arguments, ahead of the partial loads.
+    const __amdgpu_buffer_rsrc_t lens = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.seq_lens), 0, a.num_seqs * 4, kBufferWord3);
+    int len_off = s * 4;
+    asm("" : "+v"(len_off));   // a per-lane value to the compiler: no early readfirstlane
+    len_v = __builtin_amdgcn_raw_buffer_load_b32(lens, len_off, 0, 0);
+    np_load = a.n_parts;
     o_base = row * a.n_parts * kD;
     o_stride = kD;
     l_base = row * a.n_parts;
     l_stride = 1;
   }
   const float* lse = a.lse_part + l_base;
+  // partials of this row (computed where needed, after the loads it may trail)
+  auto count = [&]() {
+    if (kBalanced) return np_balanced;
+    int lv = len_v;
+    asm volatile("" : "+v"(lv));   // first use stays here, not hoisted above the loads
+    const int seq_len = min(max(lv, 0), a.max_seq_len);
+    return (seq_len + a.partition_tokens - 1) / a.partition_tokens;
+  };
+  int np;
 
   const int pl = tid >> 4;           // partition lane 0..15
   const int dl = tid & 15;           // dim lane: dims 64 quarter + 4 dl .. + 3
@@ -650,18 +726,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
 
-  if (np <= 8 * kCombinePLanes) {
+  if (np_load <= 8 * kCombinePLanes) {
     // One pass: every partition's partial and log-sum-exp are loaded at once
     // (8 per thread), then M, the weights and the sums follow.
     f32x4 x[8];
     float ls[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 8; ++u) {   // straight-line loads; p >= np_load reads partial 0
       const int p = pl + u * kCombinePLanes;
-      const bool ok = p < np;
-      x[u] = ok ? *reinterpret_cast<const f32x4*>(op + p * o_stride)
-                : f32x4{0.f, 0.f, 0.f, 0.f};
-      ls[u] = ok ? lse[p * l_stride] : -INFINITY;
+      const int pc = p < np_load ? p : 0;
+      x[u] = *reinterpret_cast<const f32x4*>(op + pc * o_stride);
+      ls[u] = lse[pc * l_stride];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before the length is used
+    np = count();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {   // partitions past this row's length hold stale data
+      const bool ok = pl + u * kCombinePLanes < np;
+      x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      ls[u] = ok ? ls[u] : -INFINITY;
     }
     float mx = ls[0];
 #pragma unroll
@@ -679,6 +762,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     }
   } else {
     // Long partition lists: M first, then chunks of weights through LDS.
+    np = count();
     float mx = -INFINITY;
     for (int p = tid; p < np; p += kCombineThreads) mx = fmaxf(mx, lse[p * l_stride]);
 #pragma unroll
@@ -754,8 +838,8 @@ __global__ __launch_bounds__(kThreads) void debug_resolve_kernel(LaunchArgs a, i
   int t = t_begin + w * kWaveTokens;
   if (t >= t_end) return;
   PageWalker walker;
-  walker.init(a.block_table + static_cast<int64_t>(c.s) * a.max_blocks, a.block_size, t, t_end,
-              lane);
+  walker.init(a.block_table + static_cast<int64_t>(c.s) * a.max_blocks, a.block_size, t,
+              PageWalker::pages_for(t_end, a.block_size), lane);
   for (;;) {
     const int nv = min(kWaveTokens, t_end - t);
     const int64_t base = walker.base(a.k_page_stride, row_stride, c.g * kD);
@@ -782,8 +866,8 @@ __global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, in
   int t = t_begin + w * kWaveTokens;
   if (t >= t_end) return;
   PageWalker walker;
-  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t, t_end,
-              lane);
+  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t,
+              PageWalker::pages_for(t_end, a.block_size), lane);
   for (;;) {
     const int nv = min(kWaveTokens, t_end - t);
     const int64_t base = walker.base(a.k_page_stride, row_stride, g * kD);
@@ -803,8 +887,10 @@ __global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, in
       VBlock vb;
       load_v_block(a.k + base, row_stride * 2, nv - 1, lane, vb);
 #pragma unroll
-      for (int i = 0; i < kWaveTokens; ++i)
-        if (i < nv) *reinterpret_cast<u32x2*>(dense_row(i) + 4 * lane) = vb.r[i];
+      for (int i = 0; i < kWaveTokens / 2; ++i) {
+        const int rr = v_row(i, lane);
+        if (rr < nv) *reinterpret_cast<u32x4*>(dense_row(rr) + 8 * (lane & 31)) = vb.r[i];
+      }
     }
     t += kTileTokens;
     if (t >= t_end) break;

@@ -109,19 +109,20 @@ def test_decode_validates_before_any_launch(lib):
 
 def test_balanced_halves_validate_before_any_launch(lib):
     fake = ctypes.c_void_p(0x10000)
-    p = params()
+    p = params(num_seqs=2)
     need = lib.pkv_decode_workspace_bytes(ctypes.byref(p))
     sb, cb = lib.pkv_split_balanced, lib.pkv_combine_balanced
-    # a fixed partition size does not select the balanced split
-    fixed = params(partition_tokens=4096)
-    assert sb(ctypes.byref(fixed), fake, fake, fake, fake, fake, fake, need, None) == -6
-    assert cb(ctypes.byref(fixed), fake, fake, need, fake, None, None) == -6
+    # a fixed partition size, or one sequence, does not select the balanced split
+    for fixed in (params(num_seqs=2, partition_tokens=4096), params(num_seqs=1)):
+        assert sb(ctypes.byref(fixed), fake, fake, fake, fake, fake, fake, need, None) == -6
+        assert cb(ctypes.byref(fixed), fake, fake, need, fake, None, None) == -6
     assert sb(ctypes.byref(p), fake, fake, fake, fake, fake, fake, need - 1, None) == -5
     assert sb(ctypes.byref(p), fake, fake, fake, fake, fake, None, need, None) == -5
     assert sb(ctypes.byref(p), None, fake, fake, fake, fake, fake, need, None) == -1
     assert cb(ctypes.byref(p), None, fake, need, fake, None, None) == -1
     assert cb(ctypes.byref(p), fake, fake, need - 1, fake, None, None) == -5
-    assert cb(ctypes.byref(params(block_size=100)), fake, fake, need, fake, None, None) == -3
+    assert cb(ctypes.byref(params(num_seqs=2, block_size=100)), fake, fake, need, fake, None,
+              None) == -3
     assert sb(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None, 0, None) == 0
 
 
@@ -153,9 +154,10 @@ def test_plan_partitions_and_workspace(lib):
     st, info = plan(lib, partition_tokens=8192, max_seq_len=8192)
     assert st == 0 and info.num_partitions == 1 and info.combine_workgroups == 0
     assert info.workspace_bytes == 0
-    # auto: pkv_decode balances; the fixed partition size reported for
-    # pkv_split / pkv_decode_partials is a multiple of 64 within [64, 4096]
-    for s, L in ((1, 8192), (8, 40000), (64, 65536), (1, 1)):
+    # auto with several sequences: pkv_decode balances; the fixed partition
+    # size reported for pkv_split / pkv_decode_partials is a multiple of 64
+    # within [64, 4096]
+    for s, L in ((2, 8192), (8, 40000), (64, 65536), (3, 1)):
         st, info = plan(lib, num_seqs=s, max_seq_len=L, max_blocks_per_seq=(L + 831) // 832)
         assert st == 0
         assert info.partition_tokens % 64 == 0 and 64 <= info.partition_tokens <= 4096
@@ -169,6 +171,17 @@ def test_plan_partitions_and_workspace(lib):
     # too many sequences for the balanced split: fixed partitions
     st, info = plan(lib, num_seqs=5000, max_seq_len=1024, max_blocks_per_seq=2)
     assert st == 0 and info.balanced == 0
+    # one sequence: fixed partitions of the automatic size, one workgroup per
+    # (KV head, partition), 256 of them for the 8192-token case
+    for L, P in ((8192, 128), (16384, 256), (32768, 512), (1, 64)):
+        st, info = plan(lib, num_seqs=1, max_seq_len=L, max_blocks_per_seq=(L + 831) // 832)
+        assert st == 0 and info.balanced == 0
+        assert info.partition_tokens == P and info.num_partitions == -(-L // P)
+        assert info.split_workgroups == 4 * info.num_partitions
+        parts = info.num_partitions
+        assert info.workspace_bytes == (0 if parts == 1 else
+                                        -(-24 * parts * 256 * 4 // 256) * 256
+                                        + -(-24 * parts * 4 // 256) * 256)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
