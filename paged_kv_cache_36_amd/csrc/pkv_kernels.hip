@@ -643,25 +643,21 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp combine: o = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M),
-// M = max_p lse_p. One workgroup per (sequence, query head, quarter of the
-// 256 dims). Pass 1 turns the partition log-sum-exps into weights in LDS
-// (chunks of kCombineChunk partitions); pass 2 has 16 partition lanes x 16
-// dim lanes (4 dims each) with 8 independent loads in flight per thread, and
-// the 16 partition lanes are summed through LDS at the end.
+// M = max_p lse_p. One wave per (sequence, query head, quarter of the 256
+// dims): lane l is partition lane l >> 4 (of 4) and dim lane l & 15 (4 dims
+// each). The partitions go in chunks of 64; a chunk's 16 partials and
+// log-sum-exps per lane are loaded at once, then folded into a running
+// maximum, weight sum and weighted sum that the 4 partition lanes share, so
+// the whole reduction stays inside the wave: no LDS, no barrier.
 // ---------------------------------------------------------------------------
-constexpr int kCombineThreads = 256;
-constexpr int kCombineChunk = 2048;
-constexpr int kCombinePLanes = 16;
+constexpr int kCombineThreads = 64;
+constexpr int kCombinePLanes = 4;
+constexpr int kCombineUnroll = 16;
+constexpr int kCombineChunk = kCombinePLanes * kCombineUnroll;   // 64 partitions
 
 template <bool kBalanced>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) {
-  __shared__ float lds_w[kCombineChunk];
-  __shared__ float lds_red[kCombineThreads / 64];
-  __shared__ f32x4 lds_acc[kCombinePLanes][16];
-
-  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
   const int quarter = blockIdx.x & 3;
   const int row_id = blockIdx.x >> 2;
@@ -710,7 +706,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     l_stride = 1;
   }
   const float* lse = a.lse_part + l_base;
-  // partials of this row (computed where needed, after the loads it may trail)
+  // partials of this row (computed after the first chunk's loads are issued)
   auto count = [&]() {
     if (kBalanced) return np_balanced;
     int lv = len_v;
@@ -718,94 +714,61 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     const int seq_len = min(max(lv, 0), a.max_seq_len);
     return (seq_len + a.partition_tokens - 1) / a.partition_tokens;
   };
-  int np;
 
-  const int pl = tid >> 4;           // partition lane 0..15
-  const int dl = tid & 15;           // dim lane: dims 64 quarter + 4 dl .. + 3
+  const int pl = lane >> 4;   // partition lane 0..3
+  const int dl = lane & 15;   // dims 64 quarter + 4 dl .. + 3
   const float* op = a.o_part + o_base + 64 * quarter + 4 * dl;
+  float m_run = -INFINITY;    // running max of the log-sum-exps seen (log2 units)
+  float den = 0.f;            // sum of weights exp2(lse2 - m_run), this lane's partitions
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-
-  if (np_load <= 8 * kCombinePLanes) {
-    // One pass: every partition's partial and log-sum-exp are loaded at once
-    // (8 per thread), then M, the weights and the sums follow.
-    f32x4 x[8];
-    float ls[8];
+  int np = 0;
+  for (int c0 = 0; c0 < np_load; c0 += kCombineChunk) {
+    f32x4 x[kCombineUnroll];
+    float ls[kCombineUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {   // straight-line loads; p >= np_load reads partial 0
-      const int p = pl + u * kCombinePLanes;
+    for (int u = 0; u < kCombineUnroll; ++u) {   // straight-line; p >= np_load reads partial 0
+      const int p = c0 + pl + u * kCombinePLanes;
       const int pc = p < np_load ? p : 0;
       x[u] = *reinterpret_cast<const f32x4*>(op + pc * o_stride);
       ls[u] = lse[pc * l_stride];
     }
     __builtin_amdgcn_sched_barrier(0);   // all loads issued before the length is used
     np = count();
+    float cm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {   // partitions past this row's length hold stale data
-      const bool ok = pl + u * kCombinePLanes < np;
+    for (int u = 0; u < kCombineUnroll; ++u) {   // partitions past the length hold stale data
+      const bool ok = c0 + pl + u * kCombinePLanes < np;
+      ls[u] = ok ? ls[u] * kLog2e : -INFINITY;
       x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
-      ls[u] = ok ? ls[u] : -INFINITY;
+      cm = fmaxf(cm, ls[u]);
     }
-    float mx = ls[0];
+    cm = fmaxf(cm, __shfl_xor(cm, 16));   // over the 4 partition lanes
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    const float m_new = fmaxf(m_run, cm);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;   // nothing seen yet: weights 0
+    const float rescale = exp2_fast(m_run - m_ref);
+    den *= rescale;
+    acc *= rescale;
 #pragma unroll
-    for (int u = 1; u < 8; ++u) mx = fmaxf(mx, ls[u]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));   // the 4 partition lanes of this wave
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (lane == 0) lds_red[w] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wgt = (pl + u * kCombinePLanes < np) ? exp2_fast((ls[u] - mx) * kLog2e) : 0.f;
-      acc += wgt * x[u];
-      if (dl == 0) den += wgt;   // one dim lane per partition lane counts the weight
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const float w = exp2_fast(ls[u] - m_ref);
+      den += w;
+      acc += w * x[u];
     }
-  } else {
-    // Long partition lists: M first, then chunks of weights through LDS.
-    np = count();
-    float mx = -INFINITY;
-    for (int p = tid; p < np; p += kCombineThreads) mx = fmaxf(mx, lse[p * l_stride]);
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
-    if (lane == 0) lds_red[w] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(lds_red[0], lds_red[1]), fmaxf(lds_red[2], lds_red[3]));
-    for (int c0 = 0; c0 < np; c0 += kCombineChunk) {
-      const int cn = min(kCombineChunk, np - c0);
-      __syncthreads();   // previous chunk's weights consumed
-      for (int p = tid; p < cn; p += kCombineThreads) {
-        const float wgt = exp2_fast((lse[(c0 + p) * l_stride] - mx) * kLog2e);
-        lds_w[p] = wgt;
-        den += wgt;
-      }
-      __syncthreads();
-      int p = pl;
-      for (; p + 7 * kCombinePLanes < cn; p += 8 * kCombinePLanes) {
-        f32x4 x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          x[u] = *reinterpret_cast<const f32x4*>(op + (c0 + p + u * kCombinePLanes) * o_stride);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += lds_w[p + u * kCombinePLanes] * x[u];
-      }
-      for (; p < cn; p += kCombinePLanes)
-        acc += lds_w[p] * *reinterpret_cast<const f32x4*>(op + (c0 + p) * o_stride);
-    }
+    m_run = m_new;
   }
-  // den: sum over all threads (each partition's weight was added once)
+  // the 4 partition lanes share m_run: plain sums finish the reduction
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) den += __shfl_xor(den, sh);
-  __syncthreads();
-  if (lane == 0) lds_red[w] = den;
-  lds_acc[pl][dl] = acc;
-  __syncthreads();
-  if (tid >= 16) return;
-  den = lds_red[0] + lds_red[1] + lds_red[2] + lds_red[3];
-  f32x4 r = lds_acc[0][tid];
-#pragma unroll
-  for (int q = 1; q < kCombinePLanes; ++q) r += lds_acc[q][tid];
-  if (np > 0) r *= 1.f / den;
-  const int64_t idx = row * kD + 64 * quarter + 4 * tid;
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+    den += __shfl_xor(den, sh);
+    acc.x += __shfl_xor(acc.x, sh);
+    acc.y += __shfl_xor(acc.y, sh);
+    acc.z += __shfl_xor(acc.z, sh);
+    acc.w += __shfl_xor(acc.w, sh);
+  }
+  if (pl != 0) return;
+  const f32x4 r = np > 0 ? acc * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t idx = row * kD + 64 * quarter + 4 * dl;
   if (a.out) {
     u32x2 packed;
     packed.x = f32_to_bf16(r.x) | (f32_to_bf16(r.y) << 16);
