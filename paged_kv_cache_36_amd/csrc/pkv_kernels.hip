@@ -474,45 +474,39 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   }
   __syncthreads();
 
-  // Every LDS value the merge needs is read first (the running maxima and
-  // sums of all waves as broadcast reads, and this thread's dim of each
-  // wave's partial), so the reads pay one latency instead of a chain of them.
+  // The weights exp2(m_w - M) / den of the 24 (head, wave) pairs are the same
+  // for every thread, so lane 4 h + w of each wave computes the one for head
+  // h and wave w (quad reductions give M and den) and every thread takes
+  // them with v_readlane: 3 transcendental instructions per wave instead of
+  // 36 per thread. Each thread then forms its dim d of the 6 outputs from
+  // the waves' partial sums in LDS.
   const int d = threadIdx.x;
-  f32x4 mv[kWaves][2], lv[kWaves][2];
   float xv[kG][kWaves];
-#pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) {
-    mv[ww][0] = *reinterpret_cast<const f32x4*>(&lds.m[ww][0]);
-    mv[ww][1] = *reinterpret_cast<const f32x4*>(&lds.m[ww][4]);
-    lv[ww][0] = *reinterpret_cast<const f32x4*>(&lds.l[ww][0]);
-    lv[ww][1] = *reinterpret_cast<const f32x4*>(&lds.l[ww][4]);
-  }
 #pragma unroll
   for (int h = 0; h < kG; ++h)
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww)
       xv[h][ww] = reinterpret_cast<const float*>(lds.v[ww])[h * kD + d];
+  const int hk = min(lane >> 2, kG - 1);   // lanes 24.. duplicate head 5
+  const int wk = lane & 3;
+  const float mk = lds.m[wk][hk];
+  const float lk = lds.l[wk][hk];
+  float mx = fmaxf(mk, __shfl_xor(mk, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  const float fk = exp2_fast(mk - mx);   // 0 for a wave without tokens
+  float den = fk * lk;
+  den += __shfl_xor(den, 1);
+  den += __shfl_xor(den, 2);
+  // den >= 1: the wave holding the maximum contributes its own weight 1
+  const float scale_k = fk * __builtin_amdgcn_rcpf(den);
+  const float lse_k = (mx + __log2f(den)) * kLn2;
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
-    float mw[kWaves], lw[kWaves];
+    float o = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      mw[ww] = mv[ww][h >> 2][h & 3];
-      lw[ww] = lv[ww][h >> 2][h & 3];
-    }
-    float mx = mw[0];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, mw[ww]);
-    float den = 0.f, num = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2_fast(mw[ww] - mx);   // 0 for a wave without tokens
-      den = fmaf(f, lw[ww], den);
-      num = fmaf(f, xv[h][ww], num);
-    }
-    // den >= 1: the wave holding the maximum contributes its own weight 1
-    const float o = num * __builtin_amdgcn_rcpf(den);
-    const float lse = (mx + __log2f(den)) * kLn2;
+    for (int ww = 0; ww < kWaves; ++ww)
+      o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scale_k), 4 * h + ww)),
+               xv[h][ww], o);
     if (target == kToOutput) {
       const int64_t idx = (head0 + h) * kD + d;
       if (a.out) a.out[idx] = static_cast<uint16_t>(f32_to_bf16(o));
@@ -521,8 +515,14 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
       const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index
                                                   : index * kG + h;
       a.o_part[prow * kD + d] = o;
-      if (d == 0) a.lse_part[prow] = lse;
     }
+  }
+  // log-sum-exps: lane 4 h of wave 0 holds head h's
+  if (target != kToOutput && w == 0 && wk == 0 && (lane >> 2) < kG) {
+    const int h = lane >> 2;
+    const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index
+                                                : index * kG + h;
+    a.lse_part[prow] = lse_k;
   }
   __syncthreads();   // LDS free for the next segment
 }
