@@ -383,7 +383,10 @@ struct SplitLds {
   alignas(16) float m[kWaves][8];
   alignas(16) float l[kWaves][8];
 };
-static_assert(kVWaveElems * 2 >= kG * kD * 4, "wave slice too small for the merge");
+// A wave's partial output in its slice during the merge: fp32 [kG][kAccStride];
+// the 16 extra floats per head put the 6 heads' rows on different LDS banks.
+constexpr int kAccStride = kD + 16;
+static_assert(kVWaveElems * 2 >= kG * kAccStride * 4, "wave slice too small for the merge");
 
 // Where a segment's result goes.
 enum SegmentTarget : int {
@@ -462,7 +465,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   const int j = lane >> 4;
   float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  float* acc_w = reinterpret_cast<float*>(lds_vw);   // this wave's slice, [kG][kD]
+  float* acc_w = reinterpret_cast<float*>(lds_vw);   // this wave's slice, [kG][kAccStride]
   if (n < kG) {
     if (j == 0) {
       lds.m[w][n] = st.m;
@@ -470,7 +473,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
     }
 #pragma unroll
     for (int db = 0; db < 16; ++db)
-      *reinterpret_cast<f32x4*>(acc_w + n * kD + 16 * db + 4 * j) = st.acc[db];
+      *reinterpret_cast<f32x4*>(acc_w + n * kAccStride + 16 * db + 4 * j) = st.acc[db];
   }
   __syncthreads();
 
@@ -486,7 +489,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   for (int h = 0; h < kG; ++h)
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww)
-      xv[h][ww] = reinterpret_cast<const float*>(lds.v[ww])[h * kD + d];
+      xv[h][ww] = reinterpret_cast<const float*>(lds.v[ww])[h * kAccStride + d];
   const int hk = min(lane >> 2, kG - 1);   // lanes 24.. duplicate head 5
   const int wk = lane & 3;
   const float mk = lds.m[wk][hk];
