@@ -39,7 +39,7 @@ COLD_BYTES = 1 << 30          # touched bytes the replicas must span
 PAGES_US = {"long_l8192_b832": 80.010, "long_l16384_b832": 122.411,
             "long_l32768_b832": 278.832}
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_36_amd", "csrc", "pkv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_decode_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_traffic.json")
 
 
 def log(msg):
@@ -314,6 +314,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": main_res["algorithmic_bytes"],
             "avg_launch_us": main_res["split_us"],
+            # the same rate against the measured streaming-read ceiling of this GPU
+            "frac_of_read_probe": round(main_res["gbps_split"] / probe, 4) if probe else None,
         },
         "cpu_baseline": cpu,
         "read_probe_gbps": probe,
