@@ -211,10 +211,74 @@ def cpu_baseline(budget_s=10.0):
             if el >= budget_s:
                 break
     us = el * 1e6 / n
+    ncpu, model = host_cpu()
     return {"value": round(us, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+            "host_cpus": ncpu, "cpu_model": model,
             "sample": f"{n} whole steps of {MAIN} (1 sequence x 8192 tokens x 24 heads, "
                       f"fp64 two-pass numpy, one thread, bf16->fp64 conversion timed), "
                       f"{el:.1f} s"}
+
+
+def host_cpu():
+    """Usable CPUs of this process and the CPU model string."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline_parallel(budget_s=10.0):
+    """The same oracle (unchanged) run in parallel over (sequence, KV head) on the
+    host's cores: each task converts its slice from bf16 and calls the oracle's
+    decode for the 6 query heads of one KV head. numpy releases the GIL inside
+    its loops, so threads run concurrently; BLAS is held to one thread each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import decode as od
+    from paged_kv_cache_36_amd import synth
+
+    case = synth.make_case(MAIN, device="cpu")
+    q_bits = case.q.view(torch.int16).numpy().view(np.uint16)
+    k_bits = case.k_logical.view(torch.int16).numpy().view(np.uint16)
+    v_bits = case.v_logical.view(torch.int16).numpy().view(np.uint16)
+    tasks = [g for g in range(k_bits.shape[1])]   # one sequence: its KV heads
+    ncpu, model = host_cpu()
+    workers = min(ncpu, len(tasks))
+
+    def task(g):
+        q = od.bf16_bits_to_f64(q_bits[0, 6 * g:6 * g + 6])
+        k = od.bf16_bits_to_f64(k_bits[:, g:g + 1])
+        v = od.bf16_bits_to_f64(v_bits[:, g:g + 1])
+        return od.attention_decode(q, k, v, case.scale)
+
+    n = 0
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(task, tasks))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    us = el * 1e6 / n
+    return {"value": round(us, 1), "unit": "us/step", "cores": workers, "kind": "oracle",
+            "host_cpus": ncpu, "cpu_model": model,
+            "sample": f"{n} whole steps of {MAIN}, {workers} threads over its KV heads "
+                      f"(the most this one-sequence step splits into), {el:.1f} s"}
 
 
 def traffic_for(res):
@@ -281,6 +345,7 @@ def main():
     log(f"read probe (2 GiB streaming read): {probe} GB/s")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel()
 
     us = main_res["us_per_step"]
     traffic = traffic_for(main_res)
@@ -318,6 +383,7 @@ def main():
             "frac_of_read_probe": round(main_res["gbps_split"] / probe, 4) if probe else None,
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
         "read_probe_gbps": probe,
         "workloads": [main_res] + extra,
     }
