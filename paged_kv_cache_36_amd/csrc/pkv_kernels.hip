@@ -383,9 +383,10 @@ struct SplitLds {
   alignas(16) float m[kWaves][8];
   alignas(16) float l[kWaves][8];
 };
-// A wave's partial output in its slice during the merge: fp32 [kG][kAccStride];
-// the 16 extra floats per head put the 6 heads' rows on different LDS banks.
-constexpr int kAccStride = kD + 16;
+// A wave's partial output in its slice during the merge: fp32 [kG][kAccStride].
+// The 4 extra floats per head start the 6 heads' rows 4 banks apart, so the
+// 16 lanes of one accumulator write (6 heads x 16 bytes) hit disjoint banks.
+constexpr int kAccStride = kD + 4;
 static_assert(kVWaveElems * 2 >= kG * kAccStride * 4, "wave slice too small for the merge");
 
 // Where a segment's result goes.
