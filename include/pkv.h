@@ -213,6 +213,50 @@ PKV_API int32_t pkv_probe_sink_floats(void);
 PKV_API pkv_status pkv_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
 PKV_API pkv_status pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * KV append: write new tokens' K and V rows into the paged caches by slot.
+ * A slot names one token row of the cache: page = slot / block_size, offset =
+ * slot % block_size ("From Attention to KV Cache Compression: Notes from a
+ * KernelGen Optimization", sections "Gather and Scatter" and "How One Output
+ * Is Produced"); the row is [num_kv_heads, head_size] inside page `page` of a
+ * [pages, block_size, num_kv_heads, head_size] cache ("海光 DCU 上的长上下文
+ * Attention：从 page784 到 page832 的 KV Cache 对齐与访存优化", §4). For a token
+ * at position t of a sequence, slot = block_table[t / B] * B + t % B (§1).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t num_tokens;     /* N new tokens (0 is a no-op)                           */
+  int32_t num_kv_heads;   /* Hkv                                                   */
+  int32_t head_size;      /* D; Hkv * D must be a multiple of 8                    */
+  int32_t block_size;     /* tokens per page, > 0                                  */
+  int64_t num_pages;      /* pages in each cache; slots >= num_pages * block_size
+                             are outside the cache and write nothing               */
+  int64_t k_page_stride;  /* elements between consecutive K pages (>= B*Hkv*D)     */
+  int64_t v_page_stride;  /* same for V (2*B*Hkv*D for the unbind view)            */
+  int64_t k_new_stride;   /* elements between consecutive new K rows (>= Hkv*D),
+                             e.g. the K slice of a fused QKV projection output      */
+  int64_t v_new_stride;   /* same for the new V rows                               */
+} pkv_append_params;
+
+/* Device inputs: k_new, v_new bf16 rows [N][Hkv*D] at the given row strides;
+ * slot_mapping int64 [N]. A negative slot marks a padding token and writes
+ * nothing. Non-negative slots must be distinct (two tokens aimed at one slot
+ * leave either row there). Device outputs: key_cache / value_cache rows at
+ * the slots, byte-exact copies. All pointers 16-byte aligned (slot_mapping
+ * 8-byte), strides multiples of 8 elements. Asynchronous on `stream`;
+ * allocates nothing; returns before any launch on a bad argument. */
+PKV_API pkv_status pkv_append(const pkv_append_params* params, const void* k_new,
+                              const void* v_new, const int64_t* slot_mapping, void* key_cache,
+                              void* value_cache, void* stream);
+
+/* Page-size rule ("海光 DCU 上的长上下文 Attention：从 page784 到 page832 的 KV Cache
+ * 对齐与访存优化", §3): the tokens per page that hold one state page of
+ * `state_page_bytes`, rounded up to a multiple of `alignment_tokens`:
+ * ceil(state_page_bytes / (alignment_tokens * attn_bytes_per_token)) *
+ * alignment_tokens. Host only. Returns -1 for a non-positive argument or a
+ * result beyond INT32_MAX. */
+PKV_API int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
+                                int32_t alignment_tokens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,13 +1,16 @@
 """Paged KV-cache single-token decode attention for AMD MI355X (gfx950).
 
 The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
-``paged_kv_cache_36_amd.api`` is its thin Python binding. ``synth`` draws the
+``paged_kv_cache_36_amd.api`` is its thin Python binding. Besides decode, the
+library writes new tokens into the paged cache (``append``) and computes the
+page-size rule (``page_tokens``). ``synth`` draws the
 seeded synthetic inputs.
 """
 
 from ._lib import LIB_PATH, LibraryMissing, load  # noqa: F401
 from .api import (  # noqa: F401
     PkvError,
+    append,
     combine,
     combine_balanced,
     debug_gather,
@@ -15,6 +18,7 @@ from .api import (  # noqa: F401
     decode,
     decode_partials,
     make_params,
+    page_tokens,
     plan,
     probe_copy,
     probe_read,

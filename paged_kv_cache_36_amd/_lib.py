@@ -46,6 +46,20 @@ class PlanInfo(ctypes.Structure):
     ]
 
 
+class AppendParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("k_page_stride", ctypes.c_int64),
+        ("v_page_stride", ctypes.c_int64),
+        ("k_new_stride", ctypes.c_int64),
+        ("v_new_stride", ctypes.c_int64),
+    ]
+
+
 _P = ctypes.POINTER(DecodeParams)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -65,6 +79,8 @@ SIGNATURES = {
     "pkv_combine_balanced": (_I32, [_P, _VP, _VP, _SZ, _VP, _VP, _VP]),
     "pkv_debug_resolve": (_I32, [_P, _I32, _VP, _VP, _VP, _VP]),
     "pkv_debug_gather": (_I32, [_P, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_append": (_I32, [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_page_tokens": (_I32, [ctypes.c_int64, ctypes.c_int64, _I32]),
     "pkv_probe_sink_floats": (_I32, []),
     "pkv_probe_read": (_I32, [_VP, _SZ, _VP, _VP]),
     "pkv_probe_copy": (_I32, [_VP, _VP, _SZ, _VP]),

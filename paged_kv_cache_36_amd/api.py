@@ -13,7 +13,7 @@ import ctypes
 
 import torch
 
-from ._lib import DecodeParams, PlanInfo, load
+from ._lib import AppendParams, DecodeParams, PlanInfo, load
 
 HEAD_SIZE = 256
 GROUP = 6
@@ -206,6 +206,50 @@ def debug_gather(params: DecodeParams, which, cache, block_table, seq_lens, fill
                                    _ptr(block_table), _ptr(seq_lens), _ptr(dense),
                                    _stream(stream)), "pkv_debug_gather")
     return dense
+
+
+def _new_rows(t: torch.Tensor, name: str, n: int, row: int) -> int:
+    """[N, Hkv, D] (or [N, Hkv*D]) bf16 with each row contiguous; rows may be spaced."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a bf16 device tensor")
+    if t.shape[0] != n or t[0].numel() != row:
+        raise ValueError(f"{name} must be [{n}, ...] with {row} elements per token, "
+                         f"got {tuple(t.shape)}")
+    inner = t[0]
+    if not inner.is_contiguous():
+        raise ValueError(f"{name}: each token row must be contiguous")
+    return t.stride(0) if n > 1 else row
+
+
+def append(k_new, v_new, slot_mapping, key_cache, value_cache, stream=None):
+    """Write the new tokens' K/V rows into the paged caches at their slots
+    (page = slot // B, offset = slot % B; negative slots are padding)."""
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    if not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous")
+    n = slot_mapping.shape[0]
+    k_stride = _page_stride(key_cache, "key_cache")
+    v_stride = _page_stride(value_cache, "value_cache")
+    if key_cache.shape != value_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    pages, bsz, hkv, d = key_cache.shape
+    p = AppendParams()
+    p.num_tokens = n
+    p.num_kv_heads = hkv
+    p.head_size = d
+    p.block_size = bsz
+    p.num_pages = pages
+    p.k_page_stride = k_stride
+    p.v_page_stride = v_stride
+    p.k_new_stride = _new_rows(k_new, "k_new", n, hkv * d) if n else hkv * d
+    p.v_new_stride = _new_rows(v_new, "v_new", n, hkv * d) if n else hkv * d
+    _check(load().pkv_append(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                             _ptr(key_cache), _ptr(value_cache), _stream(stream)), "pkv_append")
+
+
+def page_tokens(state_page_bytes: int, attn_bytes_per_token: int, alignment_tokens: int) -> int:
+    """Page-size rule: ceil(state / (alignment * bytes per token)) * alignment (host only)."""
+    return int(load().pkv_page_tokens(state_page_bytes, attn_bytes_per_token, alignment_tokens))
 
 
 def probe_sink_floats() -> int:

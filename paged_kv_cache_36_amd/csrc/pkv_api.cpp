@@ -435,4 +435,50 @@ pkv_status pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream
   return hip_status(pkv::launch_probe_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_append(const pkv_append_params* p, const void* k_new, const void* v_new,
+                      const int64_t* slot_mapping, void* key_cache, void* value_cache,
+                      void* stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (p->num_tokens < 0 || p->num_kv_heads <= 0 || p->head_size <= 0 || p->num_pages < 0)
+    return PKV_ERR_SHAPE;
+  if (p->block_size <= 0) return PKV_ERR_BLOCK_SIZE;
+  const int64_t row_elems = static_cast<int64_t>(p->num_kv_heads) * p->head_size;
+  if (row_elems % 8 != 0 || row_elems > (int64_t{1} << 20)) return PKV_ERR_UNSUPPORTED;
+  if (p->k_page_stride < p->block_size * row_elems || p->v_page_stride < p->block_size * row_elems ||
+      p->k_page_stride % 8 != 0 || p->v_page_stride % 8 != 0 || p->k_new_stride < row_elems ||
+      p->v_new_stride < row_elems || p->k_new_stride % 8 != 0 || p->v_new_stride % 8 != 0)
+    return PKV_ERR_STRIDE;
+  if (p->num_pages > (int64_t{1} << 62) / p->block_size) return PKV_ERR_SHAPE;
+  if (p->num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !key_cache || !value_cache || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(slot_mapping, 8) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16))
+    return PKV_ERR_NULL;
+  pkv::AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.slots = slot_mapping;
+  a.k_cache = static_cast<uint16_t*>(key_cache);
+  a.v_cache = static_cast<uint16_t*>(value_cache);
+  a.k_new_stride = p->k_new_stride;
+  a.v_new_stride = p->v_new_stride;
+  a.k_page_stride = p->k_page_stride;
+  a.v_page_stride = p->v_page_stride;
+  a.num_slots = p->num_pages * p->block_size;
+  a.num_tokens = p->num_tokens;
+  a.block_size = p->block_size;
+  a.row_chunks = static_cast<int32_t>(row_elems / 8);
+  return hip_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
+                        int32_t alignment_tokens) {
+  if (state_page_bytes <= 0 || attn_bytes_per_token <= 0 || alignment_tokens <= 0) return -1;
+  if (attn_bytes_per_token > INT64_MAX / alignment_tokens) return -1;
+  const int64_t unit = attn_bytes_per_token * alignment_tokens;
+  const int64_t units = state_page_bytes / unit + (state_page_bytes % unit != 0 ? 1 : 0);
+  if (units > INT32_MAX / alignment_tokens) return -1;
+  return static_cast<int32_t>(units * alignment_tokens);
+}
+
 }  // extern "C"

@@ -50,6 +50,21 @@ hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* o
                                 hipStream_t stream);
 hipError_t launch_debug_gather(const LaunchArgs& a, int32_t which, uint16_t* dense,
                                hipStream_t stream);
+// KV append: one wave per new token, rows moved as 16-byte chunks.
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* slots;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t k_new_stride, v_new_stride;   // elements
+  int64_t k_page_stride, v_page_stride; // elements
+  int64_t num_slots;                    // num_pages * block_size
+  int32_t num_tokens;
+  int32_t block_size;
+  int32_t row_chunks;                   // Hkv * D / 8
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 int32_t probe_sink_floats();
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

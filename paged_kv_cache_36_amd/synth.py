@@ -222,3 +222,27 @@ def replicate(case: Case, copies: int):
             t[s, n:] = copies * pool
         tables.append(t)
     return k_big, v_big, torch.stack(tables).to(dev)
+
+
+def append_inputs(num_tokens, block_size, num_pages, seed, *, pad_every=0, outside=0,
+                  hkv=HKV, head=HEAD, device="cpu"):
+    """Seeded inputs for the KV-append tests: a pool of random bf16 bits
+    [num_pages, B, Hkv, D], new rows [N, Hkv, D] and distinct slots drawn from
+    the pool's num_pages * B rows. Every pad_every-th token gets slot -1 and
+    the last `outside` tokens get slots past the pool. Draw order: pool,
+    rows, slot permutation. Returns (pool, rows, slots) on `device`."""
+    gen = torch.Generator().manual_seed(seed)
+    pool = torch.randint(-32768, 32768, (num_pages, block_size, hkv, head), generator=gen,
+                         dtype=torch.int32).to(torch.int16)
+    rows = torch.randint(-32768, 32768, (num_tokens, hkv, head), generator=gen,
+                         dtype=torch.int32).to(torch.int16)
+    total = num_pages * block_size
+    assert num_tokens <= total
+    slots = torch.randperm(total, generator=gen)[:num_tokens].to(torch.int64)
+    if pad_every:
+        slots[::pad_every] = -1
+    if outside:
+        slots[num_tokens - outside:] = total + torch.arange(outside, dtype=torch.int64) * 7
+    return (pool.view(torch.bfloat16).to(device), rows.view(torch.bfloat16).to(device),
+            slots.to(device))
+

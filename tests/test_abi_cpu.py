@@ -126,6 +126,67 @@ def test_balanced_halves_validate_before_any_launch(lib):
     assert sb(ctypes.byref(params(num_seqs=0)), None, None, None, None, None, None, 0, None) == 0
 
 
+def append_params(**kw):
+    p = _lib.AppendParams()
+    base = dict(num_tokens=4, num_kv_heads=4, head_size=256, block_size=832, num_pages=10,
+                k_page_stride=832 * 1024, v_page_stride=832 * 1024, k_new_stride=1024,
+                v_new_stride=1024)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_tokens=-1), -2),
+    (dict(num_kv_heads=0), -2),
+    (dict(num_pages=-1), -2),
+    (dict(block_size=0), -3),
+    (dict(head_size=3), -6),                       # row not a multiple of 8 elements
+    (dict(k_page_stride=832 * 1024 - 8), -8),
+    (dict(v_page_stride=832 * 1024 + 4), -8),
+    (dict(k_new_stride=1016), -8),
+    (dict(v_new_stride=1028), -8),
+])
+def test_append_rejects_bad_params(lib, kw, status):
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.pkv_append(ctypes.byref(append_params(**kw)), fake, fake, fake, fake, fake,
+                          None) == status
+
+
+def test_append_validates_pointers_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)
+    p = append_params()
+    ap = lib.pkv_append
+    assert ap(None, fake, fake, fake, fake, fake, None) == -1
+    assert ap(ctypes.byref(p), None, fake, fake, fake, fake, None) == -1
+    assert ap(ctypes.byref(p), fake, fake, ctypes.c_void_p(0x10004), fake, fake, None) == -1
+    assert ap(ctypes.byref(p), fake, mis, fake, fake, fake, None) == -1
+    assert ap(ctypes.byref(append_params(num_tokens=0)), None, None, None, None, None, None) == 0
+
+
+def test_page_tokens_matches_the_page_rule_fixture(lib):
+    for r in read_golden("page_size_rule.txt"):
+        assert lib.pkv_page_tokens(int(r[0]), int(r[1]), int(r[2])) == int(r[4]), r
+    assert lib.pkv_page_tokens(0, 4096, 16) == -1
+    assert lib.pkv_page_tokens(100, -1, 16) == -1
+    assert lib.pkv_page_tokens(1 << 62, 1, 64) == -1          # beyond int32
+
+
+def test_page_tokens_agrees_with_oracle_rule(lib):
+    from oracle import append as oa
+    import numpy as np
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        s = int(rng.integers(1, 1 << 40))
+        a = int(rng.integers(1, 1 << 16))
+        k = int(rng.choice([1, 8, 16, 64, 256]))
+        want = oa.page_tokens(s, a, k)
+        got = lib.pkv_page_tokens(s, a, k)
+        assert got == (want if want <= 2 ** 31 - 1 else -1), (s, a, k)
+
+
 def test_plan_page_geometry_matches_pages(lib):
     for bsz, groups, tail, _pct, page_bytes in read_golden("page_geometry.txt"):
         bsz = int(bsz)
