@@ -156,6 +156,50 @@ def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
     return res
 
 
+def measure_append(name, num_tokens, block_size, steps, warmup, torch, pkv, synth):
+    """KV append of `num_tokens` new tokens (K and V, 4 KV heads x 256) into a
+    page-832 cache: each step writes the next cold copy of the rows into its own
+    pages. Algorithmic bytes: 2 KiB read + 2 KiB written per token for each of
+    K and V."""
+    nbytes = num_tokens * 4 * 256 * 2 * 2 * 2
+    copies = max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+    rows_k, rows_v, slots, pages = synth.append_bench_inputs(num_tokens, block_size, copies,
+                                                             seed=77)
+    kc = torch.empty((pages, block_size, 4, 256), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        c = i % copies
+        pkv.append(rows_k[c], rows_v[c], slots[c], kc, vc)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    res = {"workload": name, "kernel": "append_kernel", "tokens": num_tokens,
+           "block_size": block_size, "cold_copies": copies, "steps": steps,
+           "algorithmic_bytes": nbytes, "us_per_append": round(us, 3),
+           "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "frac_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
+    log(json.dumps(res))
+    del g, rows_k, rows_v, slots, kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_probe(torch, pkv, reps=20):
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -341,6 +385,14 @@ def main():
         for name in EXTRA:
             extra.append(measure(name, min(args.steps, caps.get(name, 400)), args.warmup,
                                  torch, pkv, synth))
+    appends = []
+    if args.workloads == "all":
+        # one new token per sequence of the wide batch, and a 32768-token
+        # prefill chunk written into page-832 pages
+        appends.append(measure_append("append_decode_64tok_b832", 64, 832,
+                                      min(args.steps, 400), args.warmup, torch, pkv, synth))
+        appends.append(measure_append("append_chunk_32768tok_b832", 32768, 832,
+                                      min(args.steps, 100), args.warmup, torch, pkv, synth))
     probe = read_probe(torch, pkv)
     log(f"read probe (2 GiB streaming read): {probe} GB/s")
 
@@ -386,6 +438,7 @@ def main():
         "cpu_baseline_parallel": cpu_par,
         "read_probe_gbps": probe,
         "workloads": [main_res] + extra,
+        "append": appends,
     }
     print(json.dumps(line), flush=True)
 

@@ -246,3 +246,24 @@ def append_inputs(num_tokens, block_size, num_pages, seed, *, pad_every=0, outsi
     return (pool.view(torch.bfloat16).to(device), rows.view(torch.bfloat16).to(device),
             slots.to(device))
 
+
+def append_bench_inputs(num_tokens, block_size, copies, seed, *, hkv=HKV, head=HEAD,
+                        device="cuda"):
+    """Seeded inputs for timing KV appends on cold data: `copies` independent
+    sets of new rows [copies, N, Hkv, D] (random bf16 bits, drawn on the
+    device) and slots [copies, N] laying each copy's N tokens out as one
+    sequence over its own shuffled pages of a shared pool. Returns (rows_k,
+    rows_v, slots, num_pages)."""
+    pages_per_copy = -(-num_tokens // block_size)
+    num_pages = copies * pages_per_copy
+    gen = torch.Generator(device=device).manual_seed(seed)
+    rows_k = torch.randint(-32768, 32768, (copies, num_tokens, hkv, head), generator=gen,
+                           dtype=torch.int32, device=device).to(torch.int16).view(torch.bfloat16)
+    rows_v = torch.randint(-32768, 32768, (copies, num_tokens, hkv, head), generator=gen,
+                           dtype=torch.int32, device=device).to(torch.int16).view(torch.bfloat16)
+    cpu_gen = torch.Generator().manual_seed(seed)
+    pages = torch.randperm(num_pages, generator=cpu_gen).view(copies, pages_per_copy)
+    t = torch.arange(num_tokens, dtype=torch.int64)
+    slots = pages[:, t // block_size].to(torch.int64) * block_size + (t % block_size)
+    return rows_k, rows_v, slots.to(device), num_pages
+

@@ -91,3 +91,27 @@ def test_algorithmic_bytes_of_the_workloads():
     assert synth.make_case("tiny_l1024_b64").algorithmic_bytes() == 4206592
     assert synth.make_case("long_l8192_b832").algorithmic_bytes() == 33566720
     assert synth.make_case("batched_8seq_t131072_b832").algorithmic_bytes() == 536969216
+
+
+def test_append_inputs_are_seeded_distinct_and_in_range():
+    pool, rows, slots = synth.append_inputs(500, 64, 10, seed=4, pad_every=7, outside=3)
+    pool2, rows2, slots2 = synth.append_inputs(500, 64, 10, seed=4, pad_every=7, outside=3)
+    assert torch.equal(slots, slots2) and torch.equal(rows.view(torch.int16), rows2.view(torch.int16))
+    assert pool.shape == (10, 64, 4, 256) and rows.shape == (500, 4, 256)
+    s = slots.tolist()
+    assert all(x == -1 for x in s[:-3][::7])   # the last 3 are then moved outside
+    assert all(x >= 640 for x in s[-3:])
+    inside = [x for x in s if 0 <= x < 640]
+    assert len(inside) == len(set(inside))
+
+
+def test_append_bench_inputs_give_each_copy_its_own_pages():
+    rk, rv, slots, pages = synth.append_bench_inputs(2000, 832, 3, seed=7, device="cpu")
+    assert rk.shape == (3, 2000, 4, 256) and pages == 9
+    flat = slots.flatten().tolist()
+    assert len(set(flat)) == len(flat) and min(flat) >= 0 and max(flat) < pages * 832
+    for c in range(3):
+        used = {x // 832 for x in slots[c].tolist()}
+        assert len(used) == 3
+        others = {x // 832 for k in range(3) if k != c for x in slots[k].tolist()}
+        assert not (used & others)
