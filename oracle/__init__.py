@@ -8,7 +8,8 @@ to it; the two share no code.
 Everything here is plain numpy in float64 and follows the pages' definitions
 (the attention formula, the decode step, the paged address map, the online
 softmax recurrence). See ``oracle/decode.py`` for the per-function citations;
-``oracle/append.py`` holds the KV-append scatter and the page-size rule.
+``oracle/append.py`` holds the KV-append scatter and the page-size rule, and
+``oracle/prefill.py`` the causal tail-Q prefill over the cached sequence.
 """
 
 from .decode import (  # noqa: F401
