@@ -257,6 +257,43 @@ PKV_API pkv_status pkv_append(const pkv_append_params* params, const void* k_new
 PKV_API int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
                                 int32_t alignment_tokens);
 
+/* ------------------------------------------------------------------------
+ * Tail-Q chunked prefill of one sequence ("海光 DCU 上的长上下文 Attention：从
+ * page784 到 page832 的 KV Cache 对齐与访存优化", §6): the num_q_tokens new
+ * tokens are the last num_q_tokens of the sequence's seq_len cached tokens
+ * (their K/V rows are already in the cache, e.g. written by pkv_append).
+ * Query i sits at position seq_len - num_q_tokens + i and attends every key
+ * t <= that position (causal), query head h reading KV head h / 6:
+ * o = softmax(scale * q.K^T) . V ("From Attention to KV Cache Compression:
+ * Notes from a KernelGen Optimization", "Starting from Attention").
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t num_q_tokens;       /* Q >= 1 new tokens (the pages route Q = 1 to decode;
+                                 it is accepted here too)                          */
+  int32_t num_q_heads;        /* Hq = 6 * Hkv                                      */
+  int32_t num_kv_heads;       /* Hkv                                               */
+  int32_t head_size;          /* 256                                               */
+  int32_t block_size;         /* B tokens per page, > 0 (any size: rows are looked
+                                 up one by one)                                    */
+  int32_t max_blocks;         /* entries of block_table                            */
+  int64_t k_page_stride;      /* elements between K pages (>= B*Hkv*D)             */
+  int64_t v_page_stride;      /* same for V                                        */
+  int32_t seq_len;            /* L: cached tokens incl. the new ones,
+                                 Q <= L <= max_blocks * B                          */
+  float scale;                /* softmax scale (1/16 for D = 256)                  */
+} pkv_prefill_params;
+
+/* Device inputs: q bf16 [Q, Hq, D] contiguous; key_cache / value_cache as for
+ * pkv_decode; block_table int32 [max_blocks] (this sequence's row). Device
+ * outputs: out bf16 [Q, Hq, D] (RNE from fp32), out_f32 fp32 [Q, Hq, D] or
+ * NULL (at least one of the two). p is rounded to bf16 for the P.V product
+ * (fp32 accumulation). 16-byte aligned pointers; asynchronous on `stream`;
+ * allocates nothing; host checks return an error before any launch. */
+PKV_API pkv_status pkv_prefill(const pkv_prefill_params* params, const void* q,
+                               const void* key_cache, const void* value_cache,
+                               const int32_t* block_table, void* out, float* out_f32,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,8 +2,9 @@
 
 The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
 ``paged_kv_cache_36_amd.api`` is its thin Python binding. Besides decode, the
-library writes new tokens into the paged cache (``append``) and computes the
-page-size rule (``page_tokens``). ``synth`` draws the
+library writes new tokens into the paged cache (``append``), runs the causal
+tail-Q prefill of one sequence (``prefill``) and computes the page-size rule
+(``page_tokens``). ``synth`` draws the
 seeded synthetic inputs.
 """
 
@@ -20,6 +21,7 @@ from .api import (  # noqa: F401
     make_params,
     page_tokens,
     plan,
+    prefill,
     probe_copy,
     probe_read,
     split,

@@ -60,6 +60,21 @@ class AppendParams(ctypes.Structure):
     ]
 
 
+class PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("num_q_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_size", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("k_page_stride", ctypes.c_int64),
+        ("v_page_stride", ctypes.c_int64),
+        ("seq_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
 _P = ctypes.POINTER(DecodeParams)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -81,6 +96,7 @@ SIGNATURES = {
     "pkv_debug_gather": (_I32, [_P, _I32, _VP, _VP, _VP, _VP, _VP]),
     "pkv_append": (_I32, [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_page_tokens": (_I32, [ctypes.c_int64, ctypes.c_int64, _I32]),
+    "pkv_prefill": (_I32, [ctypes.POINTER(PrefillParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_probe_sink_floats": (_I32, []),
     "pkv_probe_read": (_I32, [_VP, _SZ, _VP, _VP]),
     "pkv_probe_copy": (_I32, [_VP, _VP, _SZ, _VP]),

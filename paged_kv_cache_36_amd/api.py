@@ -13,7 +13,7 @@ import ctypes
 
 import torch
 
-from ._lib import AppendParams, DecodeParams, PlanInfo, load
+from ._lib import AppendParams, DecodeParams, PlanInfo, PrefillParams, load
 
 HEAD_SIZE = 256
 GROUP = 6
@@ -245,6 +245,41 @@ def append(k_new, v_new, slot_mapping, key_cache, value_cache, stream=None):
     p.v_new_stride = _new_rows(v_new, "v_new", n, hkv * d) if n else hkv * d
     _check(load().pkv_append(ctypes.byref(p), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                              _ptr(key_cache), _ptr(value_cache), _stream(stream)), "pkv_append")
+
+
+def prefill(q, key_cache, value_cache, block_table, seq_len, block_size, scale, *, out=None,
+            out_f32=None, want_bf16=True, stream=None):
+    """Causal attention of one sequence's last q tokens (q: [Q, Hq, D] bf16)
+    over its seq_len cached tokens; returns (out, out_f32)."""
+    _need(q, "q", torch.bfloat16, 3)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    k_stride = _page_stride(key_cache, "key_cache")
+    v_stride = _page_stride(value_cache, "value_cache")
+    _need(block_table, "block_table", torch.int32, 1)
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    nq, hq, d = q.shape
+    _, bsz, hkv, _ = key_cache.shape
+    if bsz != block_size:
+        raise ValueError(f"block_size {block_size} does not match the cache ({bsz})")
+    if out is None and want_bf16:
+        out = torch.empty_like(q)
+    p = PrefillParams()
+    p.num_q_tokens = nq
+    p.num_q_heads = hq
+    p.num_kv_heads = hkv
+    p.head_size = d
+    p.block_size = block_size
+    p.max_blocks = block_table.shape[0]
+    p.k_page_stride = k_stride
+    p.v_page_stride = v_stride
+    p.seq_len = int(seq_len)
+    p.scale = float(scale)
+    _check(load().pkv_prefill(ctypes.byref(p), _ptr(q), _ptr(key_cache), _ptr(value_cache),
+                              _ptr(block_table), _ptr(out), _ptr(out_f32), _stream(stream)),
+           "pkv_prefill")
+    return out, out_f32
 
 
 def page_tokens(state_page_bytes: int, attn_bytes_per_token: int, alignment_tokens: int) -> int:

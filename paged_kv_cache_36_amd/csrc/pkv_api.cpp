@@ -471,6 +471,43 @@ pkv_status pkv_append(const pkv_append_params* p, const void* k_new, const void*
   return hip_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* key_cache,
+                       const void* value_cache, const int32_t* block_table, void* out,
+                       float* out_f32, void* stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (p->head_size != pkv::kHeadSize || p->num_kv_heads <= 0 ||
+      p->num_q_heads != pkv::kGroup * p->num_kv_heads)
+    return PKV_ERR_UNSUPPORTED;
+  if (p->block_size <= 0) return PKV_ERR_BLOCK_SIZE;
+  if (p->num_q_tokens < 1 || p->seq_len < p->num_q_tokens || p->max_blocks <= 0 ||
+      static_cast<int64_t>(p->seq_len) > static_cast<int64_t>(p->max_blocks) * p->block_size ||
+      !std::isfinite(p->scale))
+    return PKV_ERR_SHAPE;
+  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_size;
+  if (p->k_page_stride < p->block_size * row || p->v_page_stride < p->block_size * row ||
+      p->k_page_stride % 8 != 0 || p->v_page_stride % 8 != 0)
+    return PKV_ERR_STRIDE;
+  if (!q || !key_cache || !value_cache || !block_table || (!out && !out_f32) || !aligned(q, 16) ||
+      !aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_table, 4) ||
+      (out && !aligned(out, 16)) || (out_f32 && !aligned(out_f32, 16)))
+    return PKV_ERR_NULL;
+  pkv::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
+  a.k_page_stride = p->k_page_stride;
+  a.v_page_stride = p->v_page_stride;
+  a.num_q = p->num_q_tokens;
+  a.seq_len = p->seq_len;
+  a.num_kv_heads = p->num_kv_heads;
+  a.block_size = p->block_size;
+  a.scale_log2 = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
+  return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
                         int32_t alignment_tokens) {
   if (state_page_bytes <= 0 || attn_bytes_per_token <= 0 || alignment_tokens <= 0) return -1;

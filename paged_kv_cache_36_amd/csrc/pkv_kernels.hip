@@ -1,28 +1,29 @@
-// HIP kernels for single-token decode attention over a paged KV cache, gfx950.
+// HIP kernels for single-token decode attention over a paged KV cache, gfx950,
+// and the KV append.
 //
-// Work split. One workgroup (4 waves) owns one (sequence, partition, KV head)
-// triple; a partition is a run of P consecutive tokens of the sequence. The
-// grid enumerates the KV head fastest, so the workgroups that read the four
-// 512-byte head slices of the same 2 KiB token rows are dispatched together.
-// Inside a workgroup, wave w takes the 16-token blocks that start at
-// t_begin + 16 w + 64 k, so the workgroup streams 64-token tiles. Each wave
-// keeps its own running softmax state for the 6 query heads of the group and
-// the four states are merged once, at the end, through LDS.
+// Work split. With fixed partitions one workgroup (4 waves) owns one
+// (sequence, partition, KV head) triple, the KV head fastest in the grid so
+// the four 512-byte head slices of the same 2 KiB token rows are read
+// together. The balanced split instead gives each of 256 workgroups an even
+// share of all (sequence, KV head, 64-token tile) units. Inside a workgroup,
+// wave w takes the 16-token blocks that start at t_begin + 16 w + 64 k, so the
+// workgroup streams 64-token tiles. Each wave keeps its own running softmax
+// state for the 6 query heads of the group; the four states are merged once,
+// at the end, through LDS.
 //
 // Per 16-token block a wave
-//  - takes the block's physical page from a per-wave list of the partition's
-//    page ids (fetched once, one id per lane, read back with v_readlane), so
-//    the block table is read once per partition and never inside the loop;
-//    block sizes are multiples of 16, so a 16-token block never straddles a
-//    page and only the last block of a partition needs a tail mask,
+//  - takes the block's physical page from a per-wave list of the page ids
+//    (fetched once, one id per lane, read back with v_readlane), so the block
+//    table stays out of the loop; block sizes are multiples of 16, so a block
+//    never straddles a page and only a run's last block needs a tail mask,
 //  - loads K straight into the A-operand layout of v_mfma_f32_16x16x32_bf16
-//    (lane = token (lane & 15), 16 contiguous bytes per k-step) and V as
-//    4 dims per lane (one 512-byte row per wave instruction), both with
-//    nontemporal loads (every byte is read once), one block ahead of use,
-//  - computes the 16 x 6 scores with 8 MFMAs against the resident q fragment,
+//    (lane = token (lane & 15), 16 contiguous bytes per k-step) and V two
+//    512-byte rows per instruction (V nontemporal: every byte is read once),
+//    one block ahead of use,
+//  - computes the 16 x 6 scores with 8 MFMAs against q read from LDS,
 //  - updates (m, l) and rescales the accumulator (online softmax),
-//  - accumulates p * V in fp32 on the VALU (p is broadcast through a
-//    wave-private LDS slot).
+//  - accumulates O^T += V^T P^T with 32 v_mfma_f32_16x16x16bf16_1k: V^T is
+//    read from LDS with the transposing read, p is split into bf16 hi + lo.
 //
 // Sources: the attention formula and the decode step ("From Attention to KV
 // Cache Compression: Notes from a KernelGen Optimization", "Starting from
@@ -35,49 +36,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kD = kHeadSize;
 constexpr int kG = kGroup;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kProbeBlocks = 16384;   // read probe: 64 workgroups per CU keep enough loads in flight
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// fp32 -> bf16, round to nearest, ties to even; NaN -> canonical quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Order a wave's own LDS writes before its later LDS reads (and reads before
-// later writes). LDS requests of one wave are served in order, so only the
-// compiler has to be kept from moving them.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // ---------------------------------------------------------------------------
 // Page walker: the address of a 16-token block of one sequence.

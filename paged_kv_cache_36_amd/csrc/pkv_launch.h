@@ -65,6 +65,23 @@ struct AppendArgs {
   int32_t row_chunks;                   // Hkv * D / 8
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// Tail-Q prefill of one sequence: num_q new tokens at positions seq_len - num_q ..
+struct PrefillArgs {
+  const uint16_t* q;            // [num_q, Hq, D]
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_table;   // [max_blocks] of this sequence
+  uint16_t* out;                // bf16 [num_q, Hq, D] or null
+  float* out_f32;               // fp32 [num_q, Hq, D] or null
+  int64_t k_page_stride;
+  int64_t v_page_stride;
+  int32_t num_q;
+  int32_t seq_len;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  float scale_log2;             // scale * log2(e)
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 int32_t probe_sink_floats();
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -267,3 +267,36 @@ def append_bench_inputs(num_tokens, block_size, copies, seed, *, hkv=HKV, head=H
     slots = pages[:, t // block_size].to(torch.int64) * block_size + (t % block_size)
     return rows_k, rows_v, slots.to(device), num_pages
 
+
+# Tail-Q prefill workloads: (new tokens q, cached length L incl. them, page size).
+# q = 4096 is the pages' full prefill chunk at the three serving context tiers;
+# the last one is a shorter tail chunk.
+PREFILL_WORKLOADS = {
+    "prefill_q4096_l8192_b832": (4096, 8192, 832),
+    "prefill_q4096_l16384_b832": (4096, 16384, 832),
+    "prefill_q4096_l32768_b832": (4096, 32768, 832),
+    "prefill_q1500_l20000_b832": (1500, 20000, 832),
+}
+
+
+def build_prefill_case(name, num_q, seq_len, block_size, seed=0, device="cpu",
+                       gen_device="cpu", pool_pages=None):
+    """One sequence of seq_len cached tokens in a shuffled NaN-poisoned pool
+    (build_case) plus the queries of its last num_q tokens, q_new [Q, 24, 256]
+    bf16 N(0,1), drawn from a second generator seeded with seed + 1.
+    Returns (case, q_new)."""
+    case = build_case(name, lens=[seq_len], block_size=block_size, pool_pages=pool_pages,
+                      seed=seed, gen_device=gen_device, device=device)
+    gen = torch.Generator(device=gen_device)
+    gen.manual_seed(seed + 1)
+    q_new = _normal_bf16((num_q, HQ, HEAD), gen, gen_device, 1.0).to(device)
+    return case, q_new
+
+
+def make_prefill_case(name, device="cpu", gen_device=None, seed=None):
+    num_q, seq_len, bsz = PREFILL_WORKLOADS[name]
+    if seed is None:
+        seed = 40 + sorted(PREFILL_WORKLOADS).index(name)
+    return build_prefill_case(name, num_q, seq_len, bsz, seed=seed, device=device,
+                              gen_device=gen_device or "cpu")
+

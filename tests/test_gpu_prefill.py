@@ -1,0 +1,95 @@
+"""Tail-Q chunked prefill through the C ABI against the fp64 oracle.
+
+bf16 output: |out - ref| <= 1e-2 + 1e-2 |ref| elementwise. fp32 output: p is
+rounded to bf16 (unit roundoff 2^-9) for the P.V product while the
+denominator sums the fp32 weights, so each output element is within
+2^-9 * max|v| of the exact result (v over the row's visible keys); the test
+allows 2^-8 * max|v|.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_36_amd as pkv
+from oracle import prefill as opf
+from paged_kv_cache_36_amd import synth
+from tests.parity_util import assert_bf16_close, bits, f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected without a GPU")
+    pkv.load()
+
+
+def run_prefill(case, q_new):
+    out32 = torch.empty(q_new.shape, dtype=torch.float32, device="cuda")
+    out, _ = pkv.prefill(q_new, case.k_cache, case.v_cache, case.block_table[0],
+                         case.lens[0], case.block_size, case.scale, out_f32=out32)
+    torch.cuda.synchronize()
+    return out, out32
+
+
+def check(case, q_new, out, out32, rows=None):
+    q = f64(q_new)
+    k = f64(case.keys(0))
+    v = f64(case.values(0))
+    ref, _ = opf.attention_prefill(q, k, v, case.scale, rows=rows)
+    sel = list(range(q.shape[0])) if rows is None else sorted(set(rows))
+    got32 = f64(out32)
+    nq, length = q.shape[0], k.shape[0]
+    for i in sel:
+        p = length - nq + i
+        vmax = np.abs(v[: p + 1]).max()
+        err = np.abs(got32[i] - ref[i]).max()
+        assert err <= 2.0 ** -8 * vmax, f"query {i}: fp32 error {err:.3e} > {2.0 ** -8 * vmax:.3e}"
+    assert_bf16_close(out, ref, rows=sel, what=f"prefill Q={nq} L={length}")
+    assert torch.isfinite(out32).all()
+
+
+@pytest.mark.parametrize("nq,length,bsz", [
+    (2, 2, 64), (17, 40, 16), (128, 128, 832), (129, 300, 784), (200, 1000, 832),
+    (1, 500, 64), (333, 333, 64), (64, 4097, 784),
+])
+def test_prefill_small_full_check(nq, length, bsz):
+    print(f"[gpu] prefill Q={nq} L={length} B={bsz}", flush=True)
+    case, q_new = synth.build_prefill_case("pf", nq, length, bsz, seed=nq + length, device="cuda")
+    out, out32 = run_prefill(case, q_new)
+    check(case, q_new, out, out32)
+
+
+def test_prefill_medium_full_check():
+    print("[gpu] prefill Q=1000 L=5000 B=784", flush=True)
+    case, q_new = synth.build_prefill_case("pfm", 1000, 5000, 784, seed=3, device="cuda")
+    out, out32 = run_prefill(case, q_new)
+    check(case, q_new, out, out32)
+
+
+@pytest.mark.parametrize("name", ["prefill_q4096_l8192_b832", "prefill_q4096_l32768_b832",
+                                  "prefill_q1500_l20000_b832"])
+def test_prefill_workloads_sampled(name):
+    print(f"[gpu] prefill workload {name}", flush=True)
+    case, q_new = synth.make_prefill_case(name, device="cuda")
+    out, out32 = run_prefill(case, q_new)
+    nq = q_new.shape[0]
+    rows = sorted({0, 1, 31, 32, 127, 128, nq // 2, nq - 129, nq - 2, nq - 1})
+    check(case, q_new, out, out32, rows=rows)
+    assert torch.isfinite(out32).all()
+
+
+def test_prefill_page_size_invariant_and_repeatable():
+    outs = []
+    for bsz in (64, 784, 832):
+        case, q_new = synth.build_prefill_case("pfi", 300, 2500, bsz, seed=8, device="cuda")
+        out, _ = run_prefill(case, q_new)
+        outs.append(bits(out))
+        again, _ = run_prefill(case, q_new)
+        assert np.array_equal(bits(again), outs[-1])
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
