@@ -33,6 +33,7 @@ MAIN = "long_l8192_b832"
 EXTRA = ["long_l16384_b832", "long_l32768_b832", "ab_l32768_b784", "ab_l32768_b832",
          "batched_8seq_t131072_b832", "wide_64seq_b832_p4096"]
 PEAK_GBPS = 8000.0            # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 COLD_BYTES = 1 << 30          # touched bytes the replicas must span
 # Decode times the page832 article reports for its page-contiguous Triton kernel
 # on a Hygon DCU (gfx936), same head layout, q = 1, page 832 (context only).
@@ -196,6 +197,53 @@ def measure_append(name, num_tokens, block_size, steps, warmup, torch, pkv, synt
            "frac_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)}
     log(json.dumps(res))
     del g, rows_k, rows_v, slots, kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_flops(num_q, seq_len, hq=24, d=256):
+    """Algorithmic flops of causal tail-Q prefill: every (query, visible key,
+    head) pair costs 2 d for q.k and 2 d for p.v."""
+    pairs = num_q * (seq_len - num_q) + num_q * (num_q + 1) // 2
+    return pairs * hq * 4 * d
+
+
+def measure_prefill(name, steps, warmup, torch, pkv, synth):
+    """Tail-Q prefill of one workload, graph-replayed; bf16 MFMA-bound."""
+    case, q_new = synth.make_prefill_case(name, device="cuda")
+    nq, length = q_new.shape[0], case.lens[0]
+    flops = prefill_flops(nq, length)
+    out = torch.empty_like(q_new)
+    bt = case.block_table[0]
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        pkv.prefill(q_new, case.k_cache, case.v_cache, bt, length, case.block_size, case.scale,
+                    out=out)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    tflops = flops / (us * 1e-6) / 1e12
+    res = {"workload": name, "kernel": "prefill_kernel", "num_q": nq, "seq_len": length,
+           "block_size": case.block_size, "steps": steps, "algorithmic_flops": flops,
+           "us_per_call": round(us, 2), "tflops": round(tflops, 1),
+           "frac_peak_bf16_mfma": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    log(json.dumps(res))
+    del g, case, q_new, out
     torch.cuda.empty_cache()
     return res
 
@@ -372,7 +420,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, pkv)
 
-    if args.workloads not in ("main", "all"):
+    if args.workloads not in ("main", "all", "prefill"):
         if args.workloads not in synth.WORKLOADS:
             sys.exit(f"unknown workload {args.workloads}; choose from {sorted(synth.WORKLOADS)}")
         res = measure(args.workloads, args.steps, args.warmup, torch, pkv, synth)
@@ -393,6 +441,11 @@ def main():
                                       min(args.steps, 400), args.warmup, torch, pkv, synth))
         appends.append(measure_append("append_chunk_32768tok_b832", 32768, 832,
                                       min(args.steps, 100), args.warmup, torch, pkv, synth))
+    prefills = []
+    if args.workloads in ("all", "prefill"):
+        for name in sorted(synth.PREFILL_WORKLOADS):
+            prefills.append(measure_prefill(name, min(args.steps, 20), min(args.warmup, 3),
+                                            torch, pkv, synth))
     probe = read_probe(torch, pkv)
     log(f"read probe (2 GiB streaming read): {probe} GB/s")
 
@@ -439,6 +492,7 @@ def main():
         "read_probe_gbps": probe,
         "workloads": [main_res] + extra,
         "append": appends,
+        "prefill": prefills,
     }
     print(json.dumps(line), flush=True)
 

@@ -45,7 +45,10 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC]
     if save_temps:
+        # -save-temps=obj writes beside the output, so build into that folder
+        save_temps = os.path.abspath(save_temps)
         os.makedirs(save_temps, exist_ok=True)
+        tmp = os.path.join(save_temps, "libpkv.so.tmp")
         cmd += ["-save-temps=obj", "-o", tmp]
         cwd = save_temps
     else:
