@@ -35,6 +35,10 @@ EXTRA = ["long_l16384_b832", "long_l32768_b832", "ab_l32768_b784", "ab_l32768_b8
 PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 COLD_BYTES = 1 << 30          # touched bytes the replicas must span
+# KV appends timed next to decode: (new tokens, page size). One new token for
+# each sequence of the 64-sequence batch, and one 32768-token prefill chunk.
+APPEND_WORKLOADS = {"append_decode_64tok_b832": (64, 832),
+                    "append_chunk_32768tok_b832": (32768, 832)}
 # Decode times the page832 article reports for its page-contiguous Triton kernel
 # on a Hygon DCU (gfx936), same head layout, q = 1, page 832 (context only).
 PAGES_US = {"long_l8192_b832": 80.010, "long_l16384_b832": 122.411,
@@ -421,9 +425,17 @@ def main():
         copy_probe(torch, pkv)
 
     if args.workloads not in ("main", "all", "prefill"):
-        if args.workloads not in synth.WORKLOADS:
-            sys.exit(f"unknown workload {args.workloads}; choose from {sorted(synth.WORKLOADS)}")
-        res = measure(args.workloads, args.steps, args.warmup, torch, pkv, synth)
+        name = args.workloads
+        if name in synth.WORKLOADS:
+            res = measure(name, args.steps, args.warmup, torch, pkv, synth)
+        elif name in synth.PREFILL_WORKLOADS:
+            res = measure_prefill(name, args.steps, args.warmup, torch, pkv, synth)
+        elif name in APPEND_WORKLOADS:
+            res = measure_append(name, *APPEND_WORKLOADS[name], args.steps, args.warmup,
+                                 torch, pkv, synth)
+        else:
+            known = sorted(synth.WORKLOADS) + sorted(synth.PREFILL_WORKLOADS) + sorted(APPEND_WORKLOADS)
+            sys.exit(f"unknown workload {name}; choose from {known}")
         print(json.dumps({"workload_only": res}), flush=True)
         return
     main_res = measure(MAIN, args.steps, args.warmup, torch, pkv, synth)
@@ -437,10 +449,9 @@ def main():
     if args.workloads == "all":
         # one new token per sequence of the wide batch, and a 32768-token
         # prefill chunk written into page-832 pages
-        appends.append(measure_append("append_decode_64tok_b832", 64, 832,
-                                      min(args.steps, 400), args.warmup, torch, pkv, synth))
-        appends.append(measure_append("append_chunk_32768tok_b832", 32768, 832,
-                                      min(args.steps, 100), args.warmup, torch, pkv, synth))
+        for name, cap in (("append_decode_64tok_b832", 400), ("append_chunk_32768tok_b832", 100)):
+            appends.append(measure_append(name, *APPEND_WORKLOADS[name], min(args.steps, cap),
+                                          args.warmup, torch, pkv, synth))
     prefills = []
     if args.workloads in ("all", "prefill"):
         for name in sorted(synth.PREFILL_WORKLOADS):
