@@ -9,7 +9,9 @@ Everything here is plain numpy in float64 and follows the pages' definitions
 (the attention formula, the decode step, the paged address map, the online
 softmax recurrence). See ``oracle/decode.py`` for the per-function citations;
 ``oracle/append.py`` holds the KV-append scatter and the page-size rule, and
-``oracle/prefill.py`` the causal tail-Q prefill over the cached sequence.
+``oracle/prefill.py`` the causal tail-Q prefill over the cached sequence, and
+``oracle/compress.py`` the per-dimension softmax compression of a paged state
+window.
 """
 
 from .decode import (  # noqa: F401

@@ -300,3 +300,118 @@ def make_prefill_case(name, device="cpu", gen_device=None, seed=None):
     return build_prefill_case(name, num_q, seq_len, bsz, seed=seed, device=device,
                               gen_device=gen_device or "cpu")
 
+
+
+# ---------------------------------------------------------------------------
+# Paged window compression: state rows [values(D) | scores(D)] in fp32 blocks.
+# ---------------------------------------------------------------------------
+
+COMPRESS_HEAD = 512
+
+# The 12 shapes of the compression stage: (num_reqs, total_tokens, compress ratio).
+COMPRESS_WORKLOADS = {
+    f"compress_r{r}_t{t}_c{c}": (r, t, c)
+    for c in (128, 256, 512)
+    for r, t in ((1, 8192), (4, 32768), (8, 65536), (8, 131072))
+}
+
+
+@dataclass
+class CompressCase:
+    name: str
+    seed: int
+    states: torch.Tensor           # [T, 2D] fp32, requests back to back, rows by position
+    lens: list                     # tokens per request
+    token_to_req: torch.Tensor     # [T] int32
+    positions: torch.Tensor        # [T] int64
+    boundaries: torch.Tensor       # [N] int64 token indices
+    block_table: torch.Tensor      # [R, max_blocks] int32; padding -> the NaN block
+    state_cache: torch.Tensor      # [pool + 1, B, 2D] fp32; block `pool` is all NaN
+    block_size: int
+    compress_ratio: int
+    head_dim: int
+    pool_blocks: int
+
+    def req_range(self, r):
+        lo = sum(self.lens[:r])
+        return lo, lo + self.lens[r]
+
+    def boundaries_of(self, r):
+        lo, hi = self.req_range(r)
+        return [int(b) for b in self.boundaries.cpu().tolist() if lo <= b < hi]
+
+    @property
+    def num_outputs(self):
+        return int(self.boundaries.shape[0])
+
+
+def build_compress_case(name, num_reqs, total_tokens, compress_ratio, block_size=8, seed=0,
+                        head_dim=COMPRESS_HEAD, lens=None, boundaries="chunk_ends",
+                        gen_device="cpu", device="cpu"):
+    """Draw one compression workload and lay it out in a NaN-poisoned paged
+    state cache.
+
+    Requests get total_tokens / num_reqs tokens each (the last one the
+    remainder) unless `lens` is given; every token of a request has its
+    position 0 .. len - 1. Boundary tokens: "chunk_ends" takes every token with
+    (p + 1) % C == 0 (the windows tile each request exactly); "all" takes
+    every token (windows overlap and are cut at position 0); a list gives
+    explicit token indices. Draw order: state rows [T, 2D] fp32 N(0, 1)
+    (values then scores in each row), then a permutation of the block pool
+    (sum of ceil(len / B) plus 10 %). Request r owns the next ceil(len_r / B)
+    ids of the permutation; every other row, and one extra padding block that
+    unused table entries point to, is NaN."""
+    if lens is None:
+        base = total_tokens // num_reqs
+        lens = [base] * (num_reqs - 1) + [total_tokens - base * (num_reqs - 1)]
+    lens = [int(x) for x in lens]
+    total = sum(lens)
+    bsz, c, d = int(block_size), int(compress_ratio), int(head_dim)
+    gen = torch.Generator(device=gen_device)
+    gen.manual_seed(seed)
+    states = torch.randn((total, 2 * d), generator=gen, device=gen_device, dtype=torch.float32)
+    blocks_per_req = [-(-n // bsz) for n in lens]
+    pool = math.ceil(1.1 * sum(blocks_per_req))
+    perm = torch.randperm(pool, generator=gen, device=gen_device).cpu()
+    max_blocks = max(max(blocks_per_req), 1)
+    table = torch.full((len(lens), max_blocks), pool, dtype=torch.int32)
+    nxt = 0
+    for r, nb in enumerate(blocks_per_req):
+        table[r, :nb] = perm[nxt:nxt + nb].to(torch.int32)
+        nxt += nb
+    cache = torch.full((pool + 1, bsz, 2 * d), float("nan"), dtype=torch.float32,
+                       device=gen_device)
+    flat = cache.view(-1, 2 * d)
+    tok_req, pos = [], []
+    lo = 0
+    for r, n in enumerate(lens):
+        t = torch.arange(n, dtype=torch.int64)
+        rows = table[r, (t // bsz)].to(torch.int64) * bsz + t % bsz
+        flat[rows.to(gen_device)] = states[lo:lo + n]
+        tok_req.append(torch.full((n,), r, dtype=torch.int32))
+        pos.append(t)
+        lo += n
+    token_to_req = torch.cat(tok_req) if tok_req else torch.zeros(0, dtype=torch.int32)
+    positions = torch.cat(pos) if pos else torch.zeros(0, dtype=torch.int64)
+    if isinstance(boundaries, str):
+        if boundaries == "chunk_ends":
+            bnd = torch.nonzero((positions + 1) % c == 0).flatten()
+        elif boundaries == "all":
+            bnd = torch.arange(total, dtype=torch.int64)
+        else:
+            raise ValueError(boundaries)
+    else:
+        bnd = torch.as_tensor(boundaries, dtype=torch.int64)
+    return CompressCase(name=name, seed=seed, states=states.to(device), lens=lens,
+                        token_to_req=token_to_req.to(device), positions=positions.to(device),
+                        boundaries=bnd.to(torch.int64).to(device), block_table=table.to(device),
+                        state_cache=cache.to(device), block_size=bsz, compress_ratio=c,
+                        head_dim=d, pool_blocks=pool)
+
+
+def make_compress_case(name, device="cpu", gen_device=None, seed=None):
+    num_reqs, total, c = COMPRESS_WORKLOADS[name]
+    if seed is None:
+        seed = 60 + sorted(COMPRESS_WORKLOADS).index(name)
+    return build_compress_case(name, num_reqs, total, c, block_size=8, seed=seed,
+                               gen_device=gen_device or "cpu", device=device)
