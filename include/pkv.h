@@ -294,6 +294,61 @@ PKV_API pkv_status pkv_prefill(const pkv_prefill_params* params, const void* q,
                                const int32_t* block_table, void* out, float* out_f32,
                                void* stream);
 
+/* ------------------------------------------------------------------------
+ * Paged window compression ("From Attention to KV Cache Compression: Notes
+ * from a KernelGen Optimization", "The Compression Operator", "How One Output
+ * Is Produced"): for every boundary token b, with request r = token_to_req[b]
+ * and position p = positions[b], the window is positions t = p - C + 1 .. p of
+ * request r (cut at 0; the page's workloads have p >= C - 1). Position t reads
+ * state row o = t % B of block block_table[r, t / B]; its first D = 512 floats
+ * are values v_t and the next 512 scores s_t. The output, per dimension d:
+ *   compressed[n, d] = sum_t softmax_t(s_{t,d}) v_{t,d}   (over the window).
+ * A dimension whose window scores are all -inf gives 0. Only this reduction
+ * stage is built; RMSNorm, INT8 quantisation, RoPE and the byte scatter of
+ * the page's finalizer are not.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t num_outputs;     /* N boundary tokens (0 is a no-op)                     */
+  int32_t num_tokens;      /* T entries of token_to_req and positions (>= 1 when
+                              N > 0)                                               */
+  int32_t num_reqs;        /* R rows of block_table                                */
+  int32_t max_blocks;      /* entries per block_table row; max_blocks * B must not
+                              exceed INT32_MAX                                     */
+  int32_t head_dim;        /* D: 512 (a state row holds 2 D floats)               */
+  int32_t block_size;      /* B state rows per block, > 0 (8 on the page)          */
+  int32_t compress_ratio;  /* C window length, >= 1 (128, 256, 512 on the page)    */
+  int32_t num_splits;      /* 0: the library chooses; else S window parts per
+                              output, 1 <= S <= C, each touching at most 64 blocks
+                              (ceil((ceil(C/S) - 1) / B) + 1 <= 64)                */
+  int64_t block_stride;    /* elements between state blocks (>= B * row_stride)    */
+  int64_t row_stride;      /* elements between rows of a block (>= 2 D), multiple
+                              of 4                                                 */
+} pkv_compress_params;
+
+/* Window parts per output the library would use (num_splits resolved), or a
+ * negative pkv_status for invalid params. Host only. */
+PKV_API int32_t pkv_compress_splits(const pkv_compress_params* params);
+
+/* Device workspace bytes pkv_compress needs (0 when one part covers each
+ * window; else N * S * D * 8 bytes of fp32 partials). Host only; 0 for invalid
+ * params. */
+PKV_API size_t pkv_compress_workspace_bytes(const pkv_compress_params* params);
+
+/* Device inputs: state_cache fp32 at the given strides (16-byte aligned);
+ * token_to_req int32 [T]; positions int64 [T]; boundary_token_indices int64
+ * [N]; block_table int32 [R, max_blocks]. Device output: compressed fp32
+ * [N, D] (16-byte aligned). Workspace: pkv_compress_workspace_bytes(params)
+ * bytes, 256-byte aligned, or NULL when that is 0. A boundary index outside
+ * [0, T), a request outside [0, R), a negative position or one whose block
+ * lies past max_blocks gives a NaN row and reads nothing else; block-table
+ * entries are trusted. Asynchronous on `stream`; allocates nothing; host
+ * checks return an error before any launch. */
+PKV_API pkv_status pkv_compress(const pkv_compress_params* params, const float* state_cache,
+                                const int32_t* token_to_req, const int64_t* positions,
+                                const int64_t* boundary_token_indices, const int32_t* block_table,
+                                float* compressed, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,9 +3,9 @@
 The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
 ``paged_kv_cache_36_amd.api`` is its thin Python binding. Besides decode, the
 library writes new tokens into the paged cache (``append``), runs the causal
-tail-Q prefill of one sequence (``prefill``) and computes the page-size rule
-(``page_tokens``). ``synth`` draws the
-seeded synthetic inputs.
+tail-Q prefill of one sequence (``prefill``), compresses windows of a paged
+state cache (``compress``) and computes the page-size rule (``page_tokens``).
+``synth`` draws the seeded synthetic inputs.
 """
 
 from ._lib import LIB_PATH, LibraryMissing, load  # noqa: F401
@@ -14,6 +14,9 @@ from .api import (  # noqa: F401
     append,
     combine,
     combine_balanced,
+    compress,
+    compress_params,
+    compress_splits,
     debug_gather,
     debug_resolve,
     decode,

@@ -75,6 +75,21 @@ class PrefillParams(ctypes.Structure):
     ]
 
 
+class CompressParams(ctypes.Structure):
+    _fields_ = [
+        ("num_outputs", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("compress_ratio", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("block_stride", ctypes.c_int64),
+        ("row_stride", ctypes.c_int64),
+    ]
+
+
 _P = ctypes.POINTER(DecodeParams)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -97,6 +112,10 @@ SIGNATURES = {
     "pkv_append": (_I32, [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_page_tokens": (_I32, [ctypes.c_int64, ctypes.c_int64, _I32]),
     "pkv_prefill": (_I32, [ctypes.POINTER(PrefillParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_compress_splits": (_I32, [ctypes.POINTER(CompressParams)]),
+    "pkv_compress_workspace_bytes": (_SZ, [ctypes.POINTER(CompressParams)]),
+    "pkv_compress": (_I32, [ctypes.POINTER(CompressParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                            _SZ, _VP]),
     "pkv_probe_sink_floats": (_I32, []),
     "pkv_probe_read": (_I32, [_VP, _SZ, _VP, _VP]),
     "pkv_probe_copy": (_I32, [_VP, _VP, _SZ, _VP]),

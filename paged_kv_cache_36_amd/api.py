@@ -13,7 +13,7 @@ import ctypes
 
 import torch
 
-from ._lib import AppendParams, DecodeParams, PlanInfo, PrefillParams, load
+from ._lib import AppendParams, CompressParams, DecodeParams, PlanInfo, PrefillParams, load
 
 HEAD_SIZE = 256
 GROUP = 6
@@ -280,6 +280,64 @@ def prefill(q, key_cache, value_cache, block_table, seq_len, block_size, scale, 
                               _ptr(block_table), _ptr(out), _ptr(out_f32), _stream(stream)),
            "pkv_prefill")
     return out, out_f32
+
+
+def compress_params(state_cache, token_to_req, boundary_token_indices, block_table,
+                    compress_ratio, num_splits=0):
+    """pkv_compress_params for a state cache [blocks, B, 2D] (fp32, any block
+    stride, rows contiguous within a block)."""
+    _need(state_cache, "state_cache", torch.float32, 3)
+    nblk, bsz, row = state_cache.shape
+    if state_cache.stride(2) != 1 or state_cache.stride(1) != row:
+        raise ValueError("state_cache rows must be contiguous within a block")
+    p = CompressParams()
+    p.num_outputs = boundary_token_indices.shape[0]
+    p.num_tokens = token_to_req.shape[0]
+    p.num_reqs = block_table.shape[0]
+    p.max_blocks = block_table.shape[1]
+    p.head_dim = row // 2
+    p.block_size = bsz
+    p.compress_ratio = int(compress_ratio)
+    p.num_splits = int(num_splits)
+    p.block_stride = state_cache.stride(0)
+    p.row_stride = state_cache.stride(1)
+    return p
+
+
+def compress_splits(p) -> int:
+    return int(load().pkv_compress_splits(ctypes.byref(p)))
+
+
+def compress(state_cache, token_to_req, positions, boundary_token_indices, block_table,
+             compress_ratio, *, num_splits=0, out=None, workspace=None, stream=None):
+    """Per-dimension softmax compression of each boundary token's window of
+    paged state rows; returns compressed fp32 [N, D] (allocated with torch
+    when not given, as is the workspace)."""
+    _need(token_to_req, "token_to_req", torch.int32, 1)
+    _need(positions, "positions", torch.int64, 1)
+    _need(boundary_token_indices, "boundary_token_indices", torch.int64, 1)
+    _need(block_table, "block_table", torch.int32, 2)
+    for t, name in ((token_to_req, "token_to_req"), (positions, "positions"),
+                    (boundary_token_indices, "boundary_token_indices"),
+                    (block_table, "block_table")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if positions.shape[0] != token_to_req.shape[0]:
+        raise ValueError("positions and token_to_req differ in length")
+    p = compress_params(state_cache, token_to_req, boundary_token_indices, block_table,
+                        compress_ratio, num_splits)
+    n = p.num_outputs
+    if out is None:
+        out = torch.empty((n, p.head_dim), dtype=torch.float32, device=state_cache.device)
+    need = int(load().pkv_compress_workspace_bytes(ctypes.byref(p)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=state_cache.device)
+    _check(load().pkv_compress(ctypes.byref(p), _ptr(state_cache), _ptr(token_to_req),
+                               _ptr(positions), _ptr(boundary_token_indices), _ptr(block_table),
+                               _ptr(out), _ptr(workspace),
+                               0 if workspace is None else workspace.numel(), _stream(stream)),
+           "pkv_compress")
+    return out
 
 
 def page_tokens(state_page_bytes: int, attn_bytes_per_token: int, alignment_tokens: int) -> int:

@@ -508,6 +508,98 @@ pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* k
   return hip_status(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Window parts per output: the caller's S, else the smallest power of two that
+// gives at least 1024 workgroups while parts keep 16 rows or more. Every part
+// must touch at most kCompressMaxBlocks logical blocks (its ids sit one per
+// lane). Returns a negative status for invalid params.
+int32_t compress_splits(const pkv_compress_params* p) {
+  if (!p) return PKV_ERR_NULL;
+  if (p->head_dim != pkv::kCompressDim) return PKV_ERR_UNSUPPORTED;
+  if (p->block_size <= 0) return PKV_ERR_BLOCK_SIZE;
+  if (p->num_outputs < 0 || p->num_tokens < 0 || p->num_reqs < 0 || p->max_blocks < 0 ||
+      p->compress_ratio < 1 || (p->num_outputs > 0 && (p->num_tokens < 1 || p->num_reqs < 1 ||
+                                                        p->max_blocks < 1)) ||
+      static_cast<int64_t>(p->max_blocks) * p->block_size > INT32_MAX)
+    return PKV_ERR_SHAPE;
+  if (p->row_stride < 2 * p->head_dim || p->row_stride % 4 != 0 ||
+      p->block_stride < p->block_size * p->row_stride || p->block_stride % 4 != 0)
+    return PKV_ERR_STRIDE;
+  const int64_t c = p->compress_ratio;
+  auto blocks_touched = [&](int64_t s) {
+    const int64_t rows = (c + s - 1) / s;
+    return (rows - 1 + p->block_size - 1) / p->block_size + 1;
+  };
+  int64_t s = p->num_splits;
+  if (s < 0 || s > c) return PKV_ERR_PARTITION;
+  if (s > 0) {
+    if (blocks_touched(s) > pkv::kCompressMaxBlocks) return PKV_ERR_PARTITION;
+  } else {
+    s = 1;
+    while (blocks_touched(s) > pkv::kCompressMaxBlocks) s *= 2;
+    while (static_cast<int64_t>(p->num_outputs) * s < 1024 && (c + 2 * s - 1) / (2 * s) >= 16)
+      s *= 2;
+    if (s > c) s = c;
+  }
+  if (static_cast<int64_t>(p->num_outputs) * s > INT32_MAX) return PKV_ERR_SHAPE;
+  return static_cast<int32_t>(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_compress_splits(const pkv_compress_params* params) { return compress_splits(params); }
+
+size_t pkv_compress_workspace_bytes(const pkv_compress_params* params) {
+  const int32_t s = compress_splits(params);
+  if (s <= 1) return 0;
+  const size_t part = static_cast<size_t>(params->num_outputs) * s * pkv::kCompressDim * 4;
+  return 2 * ((part + 255) / 256 * 256);
+}
+
+pkv_status pkv_compress(const pkv_compress_params* p, const float* state_cache,
+                        const int32_t* token_to_req, const int64_t* positions,
+                        const int64_t* boundary_token_indices, const int32_t* block_table,
+                        float* compressed, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const int32_t s = compress_splits(p);
+  if (s < 0) return static_cast<pkv_status>(s);
+  if (p->num_outputs == 0) return PKV_OK;
+  if (!state_cache || !token_to_req || !positions || !boundary_token_indices || !block_table ||
+      !compressed || !aligned(state_cache, 16) || !aligned(compressed, 16) ||
+      !aligned(token_to_req, 4) || !aligned(positions, 8) || !aligned(boundary_token_indices, 8) ||
+      !aligned(block_table, 4))
+    return PKV_ERR_NULL;
+  const size_t need = pkv_compress_workspace_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PKV_ERR_WORKSPACE;
+  pkv::CompressArgs a;
+  a.state = state_cache;
+  a.token_to_req = token_to_req;
+  a.positions = positions;
+  a.boundaries = boundary_token_indices;
+  a.block_table = block_table;
+  a.out = compressed;
+  a.o_part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.lse_part = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2)
+                        : nullptr;
+  a.block_stride = p->block_stride;
+  a.row_stride = p->row_stride;
+  a.num_outputs = p->num_outputs;
+  a.num_tokens = p->num_tokens;
+  a.num_reqs = p->num_reqs;
+  a.max_blocks = p->max_blocks;
+  a.block_size = p->block_size;
+  a.compress_ratio = p->compress_ratio;
+  a.num_splits = s;
+  a.part_rows = (p->compress_ratio + s - 1) / s;
+  return hip_status(pkv::launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
                         int32_t alignment_tokens) {
   if (state_page_bytes <= 0 || attn_bytes_per_token <= 0 || alignment_tokens <= 0) return -1;

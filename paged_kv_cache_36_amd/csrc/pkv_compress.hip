@@ -1,0 +1,265 @@
+// HIP kernels for the paged window compression stage, gfx950.
+//
+// For every boundary token b (request r, position p) the window is positions
+// p - C + 1 .. p of request r (cut at 0); each position t reads state row
+// block_table[r, t / B] * B + t % B, whose first D = 512 floats are values v
+// and next 512 are scores s. Per dimension d the output is
+// c_d = sum_i softmax_i(s_{i,d}) v_{i,d} over the window ("From Attention to
+// KV Cache Compression: Notes from a KernelGen Optimization", "How One Output
+// Is Produced"), computed with the running maximum / denominator / numerator
+// of the same page's "Online Softmax: Streaming Away the Window".
+//
+// Work split. A window is cut into num_splits parts of part_rows rows; one
+// workgroup (4 waves) takes one (output, part). Wave w handles dimension half
+// w & 1 (lane l: dims 256 (w & 1) + 4 l .. + 3, one 16-byte load of values and
+// one of scores per row, so a wave instruction reads 1 KiB contiguous) and the
+// part's 8-row batches w >> 1, (w >> 1) + 2, ...; the next batch is loaded
+// while the current one is reduced. The part's physical block ids are loaded
+// once (lane i: the part's i-th logical block) and each row takes its id with
+// v_readlane. The two row phases merge through LDS. A single part writes c
+// directly; several write (c_p, log2-sum-exp_p) per dimension and the combine
+// kernel merges them.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kCmpThreads = 256;
+constexpr int kCmpBatch = 8;                  // rows per batch
+constexpr int kCmpHalf = kCompressDim / 2;    // dims per wave
+
+struct CmpState {
+  float m[4];     // running max, log2 units
+  float den[4];
+  float num[4];
+};
+
+struct CmpLds {
+  f32x4 m[2][64];
+  f32x4 den[2][64];
+  f32x4 num[2][64];
+};
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArgs a) {
+  __shared__ CmpLds lds;
+  const int n = blockIdx.x / a.num_splits;
+  const int part = blockIdx.x - n * a.num_splits;
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int half = w & 1;
+  const int phase = w >> 1;
+
+  // Boundary token -> (request, position). Indices outside their arrays make
+  // the output NaN instead of reading out of bounds.
+  const int64_t b = a.boundaries[n];
+  bool ok = b >= 0 && b < a.num_tokens;
+  const int64_t bs = ok ? b : 0;
+  const int r = a.token_to_req[bs];
+  const int64_t p = a.positions[bs];
+  ok = ok && r >= 0 && r < a.num_reqs && p >= 0 && p / a.block_size < a.max_blocks;
+
+  // The part's positions [ts, ts + nrows): window rows part * R .. part * R +
+  // R - 1. A valid p is below max_blocks * B <= INT32_MAX, so 32 bits hold it.
+  const int p32 = ok ? static_cast<int>(p) : 0;
+  const int lo = p32 - a.compress_ratio + 1 + part * a.part_rows;
+  const int hi = min(lo + a.part_rows, p32 + 1);
+  const int ts = max(lo, 0);
+  const int nrows = ok ? max(hi - ts, 0) : 0;
+
+  // The part's physical block ids: lane i holds logical block lb0 + i. The
+  // load is retired here, on every path, so that the waits the compiler
+  // places inside the batch loop never hold back a prefetched batch.
+  const int lb0 = ts / a.block_size;
+  const int o0 = ts - lb0 * a.block_size;
+  int blk = 0;
+  if (nrows > 0) {
+    const int lb_last = (ts + nrows - 1) / a.block_size;
+    if (lane <= lb_last - lb0)
+      blk = a.block_table[static_cast<int64_t>(r) * a.max_blocks + lb0 + lane];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): expcnt and lgkmcnt left at their maxima
+  const int64_t first = static_cast<int64_t>(__builtin_amdgcn_readlane(blk, 0)) * a.block_stride +
+                        static_cast<int64_t>(o0) * a.row_stride;
+
+  const float* base = a.state + kCmpHalf * half + 4 * lane;
+  const int nbatch = (nrows + kCmpBatch - 1) / kCmpBatch;
+
+  // (logical block - lb0, offset) of the wave's next row, walked forward: the
+  // wave's batches are every other 8-row batch of the part.
+  int lb = 0, o = o0;
+  auto skip_rows = [&](int rows) {
+    o += rows;
+    while (o >= a.block_size) {
+      o -= a.block_size;
+      ++lb;
+    }
+  };
+  skip_rows(kCmpBatch * phase);
+
+  // Row offsets (elements) of batch k, which starts at the walker; rows past
+  // the part repeat its first row (their scores are then set to -inf).
+  auto row_offsets = [&](int k, int64_t (&off)[kCmpBatch]) {
+#pragma unroll
+    for (int i = 0; i < kCmpBatch; ++i) {
+      const bool valid = k * kCmpBatch + i < nrows;
+      const int page = __builtin_amdgcn_readlane(blk, valid ? lb : 0);
+      off[i] = valid ? static_cast<int64_t>(page) * a.block_stride +
+                           static_cast<int64_t>(o) * a.row_stride
+                     : first;
+      skip_rows(1);
+    }
+    skip_rows(kCmpBatch);   // the other phase's batch
+  };
+  auto load = [&](int k, f32x4 (&v)[kCmpBatch], f32x4 (&s)[kCmpBatch]) {
+    int64_t off[kCmpBatch];
+    row_offsets(k, off);
+#pragma unroll
+    for (int i = 0; i < kCmpBatch; ++i) {
+      v[i] = ld4(base + off[i]);
+      s[i] = ld4(base + off[i] + kCompressDim);
+    }
+  };
+
+  CmpState st;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    st.m[d] = -INFINITY;
+    st.den[d] = 0.f;
+    st.num[d] = 0.f;
+  }
+  auto consume = [&](int k, const f32x4 (&v)[kCmpBatch], f32x4 (&s)[kCmpBatch]) {
+    const int valid = nrows - k * kCmpBatch;
+    if (valid < kCmpBatch) {   // the part's last batch only
+#pragma unroll
+      for (int i = 0; i < kCmpBatch; ++i)
+        if (i >= valid) s[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float bm = s[0][d];
+#pragma unroll
+      for (int i = 1; i < kCmpBatch; ++i) bm = fmaxf(bm, s[i][d]);
+      const float mn = fmaxf(st.m[d], bm * kLog2e);
+      const float mref = mn == -INFINITY ? 0.f : mn;   // nothing finite yet: weights 0
+      const float alpha = exp2_fast(st.m[d] - mref);
+      float ds = 0.f, ns = 0.f;
+#pragma unroll
+      for (int i = 0; i < kCmpBatch; ++i) {
+        const float e = exp2_fast(__builtin_fmaf(s[i][d], kLog2e, -mref));
+        ds += e;
+        ns = __builtin_fmaf(e, v[i][d], ns);
+      }
+      st.den[d] = __builtin_fmaf(st.den[d], alpha, ds);
+      st.num[d] = __builtin_fmaf(st.num[d], alpha, ns);
+      st.m[d] = mn;
+    }
+  };
+
+  // Batches phase, phase + 2, ...: two in flight. The prefetch is issued
+  // unconditionally (past the part it re-reads the part's first row) so that
+  // the loop body has one path and its waits count only the batch consumed.
+  f32x4 va[kCmpBatch], sa[kCmpBatch], vb[kCmpBatch], sb[kCmpBatch];
+  int k = phase;
+  if (k < nbatch) {
+    load(k, va, sa);
+    for (;;) {
+      load(k + 2, vb, sb);
+      consume(k, va, sa);
+      k += 2;
+      if (k >= nbatch) break;
+      load(k + 2, va, sa);
+      consume(k, vb, sb);
+      k += 2;
+      if (k >= nbatch) break;
+    }
+  }
+
+  // merge the two row phases of each dimension half
+  if (phase == 1) {
+    lds.m[half][lane] = f32x4{st.m[0], st.m[1], st.m[2], st.m[3]};
+    lds.den[half][lane] = f32x4{st.den[0], st.den[1], st.den[2], st.den[3]};
+    lds.num[half][lane] = f32x4{st.num[0], st.num[1], st.num[2], st.num[3]};
+  }
+  __syncthreads();
+  if (phase == 1) return;
+  const f32x4 m1 = lds.m[half][lane];
+  const f32x4 d1 = lds.den[half][lane];
+  const f32x4 n1 = lds.num[half][lane];
+  f32x4 c, lse;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float mt = fmaxf(st.m[d], m1[d]);
+    const float mref = mt == -INFINITY ? 0.f : mt;
+    const float w0 = exp2_fast(st.m[d] - mref);
+    const float w1 = exp2_fast(m1[d] - mref);
+    const float den = st.den[d] * w0 + d1[d] * w1;
+    const float num = st.num[d] * w0 + n1[d] * w1;
+    c[d] = den > 0.f ? num / den : 0.f;
+    lse[d] = den > 0.f ? mt + __log2f(den) : -INFINITY;
+    if (!ok) {
+      c[d] = __builtin_nanf("");
+      lse[d] = INFINITY;
+    }
+  }
+  const int dim = kCmpHalf * half + 4 * lane;
+  if (a.num_splits == 1) {
+    *reinterpret_cast<f32x4*>(a.out + static_cast<int64_t>(n) * kCompressDim + dim) = c;
+  } else {
+    const int64_t idx = (static_cast<int64_t>(n) * a.num_splits + part) * kCompressDim + dim;
+    *reinterpret_cast<f32x4*>(a.o_part + idx) = c;
+    *reinterpret_cast<f32x4*>(a.lse_part + idx) = lse;
+  }
+}
+
+// One thread per (output, dimension): c = sum_p 2^(lse_p - LSE) c_p with the
+// maximum taken first. An output whose parts all carry lse = +inf (bad
+// indices) comes out NaN; one with no finite score comes out 0.
+__global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressArgs a) {
+  const int per_out = kCompressDim / kCmpThreads;
+  const int n = blockIdx.x / per_out;
+  const int dim = (blockIdx.x - n * per_out) * kCmpThreads + threadIdx.x;
+  const int64_t base = static_cast<int64_t>(n) * a.num_splits * kCompressDim + dim;
+  float mt = -INFINITY;
+  for (int j = 0; j < a.num_splits; ++j) mt = fmaxf(mt, a.lse_part[base + j * kCompressDim]);
+  float c = 0.f;
+  if (mt != -INFINITY) {
+    float tot = 0.f, acc = 0.f;
+    for (int j = 0; j < a.num_splits; ++j) {
+      const float l = a.lse_part[base + j * kCompressDim];
+      const float o = a.o_part[base + j * kCompressDim];
+      const float wgt = exp2_fast(l - mt);
+      if (wgt > 0.f) {   // parts without rows carry c = 0 and weight 0
+        tot += wgt;
+        acc = __builtin_fmaf(wgt, o, acc);
+      } else if (wgt != wgt) {
+        tot = __builtin_nanf("");
+      }
+    }
+    c = acc / tot;
+  }
+  a.out[static_cast<int64_t>(n) * kCompressDim + dim] = c;
+}
+
+}  // namespace
+
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
+  if (a.num_outputs <= 0) return hipSuccess;
+  const int64_t blocks = static_cast<int64_t>(a.num_outputs) * a.num_splits;
+  hipLaunchKernelGGL(compress_split_kernel, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kCmpThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const int64_t cblocks = static_cast<int64_t>(a.num_outputs) * (kCompressDim / kCmpThreads);
+  hipLaunchKernelGGL(compress_combine_kernel, dim3(static_cast<uint32_t>(cblocks)),
+                     dim3(kCmpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

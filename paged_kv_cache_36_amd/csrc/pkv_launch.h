@@ -82,6 +82,32 @@ struct PrefillArgs {
   float scale_log2;             // scale * log2(e)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Paged window compression: per-dimension softmax over each boundary token's
+// window of state rows [values(D) | scores(D)], fp32, D = kCompressDim.
+constexpr int kCompressDim = 512;
+constexpr int kCompressMaxBlocks = 64;   // logical blocks one window part may touch
+struct CompressArgs {
+  const float* state;             // paged state cache
+  const int32_t* token_to_req;    // [num_tokens]
+  const int64_t* positions;       // [num_tokens]
+  const int64_t* boundaries;      // [num_outputs] token indices
+  const int32_t* block_table;     // [num_reqs, max_blocks]
+  float* out;                     // [num_outputs, D]
+  float* o_part;                  // [num_outputs, num_splits, D] (num_splits > 1)
+  float* lse_part;                // same shape, log2 units
+  int64_t block_stride;           // elements between state blocks
+  int64_t row_stride;             // elements between rows of a block
+  int32_t num_outputs;
+  int32_t num_tokens;
+  int32_t num_reqs;
+  int32_t max_blocks;
+  int32_t block_size;
+  int32_t compress_ratio;
+  int32_t num_splits;             // window parts per output
+  int32_t part_rows;              // ceil(compress_ratio / num_splits)
+};
+// split kernel, then (num_splits > 1) the combine kernel
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
 int32_t probe_sink_floats();
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

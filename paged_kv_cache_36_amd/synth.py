@@ -347,7 +347,7 @@ class CompressCase:
 
 def build_compress_case(name, num_reqs, total_tokens, compress_ratio, block_size=8, seed=0,
                         head_dim=COMPRESS_HEAD, lens=None, boundaries="chunk_ends",
-                        gen_device="cpu", device="cpu"):
+                        gen_device="cpu", device="cpu", states_fn=None):
     """Draw one compression workload and lay it out in a NaN-poisoned paged
     state cache.
 
@@ -360,7 +360,8 @@ def build_compress_case(name, num_reqs, total_tokens, compress_ratio, block_size
     (values then scores in each row), then a permutation of the block pool
     (sum of ceil(len / B) plus 10 %). Request r owns the next ceil(len_r / B)
     ids of the permutation; every other row, and one extra padding block that
-    unused table entries point to, is NaN."""
+    unused table entries point to, is NaN. `states_fn(states, positions)`, if
+    given, may rewrite the drawn rows in place before they are laid out."""
     if lens is None:
         base = total_tokens // num_reqs
         lens = [base] * (num_reqs - 1) + [total_tokens - base * (num_reqs - 1)]
@@ -370,6 +371,8 @@ def build_compress_case(name, num_reqs, total_tokens, compress_ratio, block_size
     gen = torch.Generator(device=gen_device)
     gen.manual_seed(seed)
     states = torch.randn((total, 2 * d), generator=gen, device=gen_device, dtype=torch.float32)
+    if states_fn is not None:
+        states_fn(states, torch.cat([torch.arange(n, dtype=torch.int64) for n in lens]))
     blocks_per_req = [-(-n // bsz) for n in lens]
     pool = math.ceil(1.1 * sum(blocks_per_req))
     perm = torch.randperm(pool, generator=gen, device=gen_device).cpu()

@@ -250,3 +250,54 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.load()
+
+
+# ------------------------------------------------------------ compression planner
+
+def cparams(**kw):
+    p = _lib.CompressParams()
+    base = dict(num_outputs=64, num_tokens=8192, num_reqs=1, max_blocks=1024, head_dim=512,
+                block_size=8, compress_ratio=128, num_splits=0, block_stride=8 * 1024,
+                row_stride=1024)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_compress_splits_auto_and_limits(lib):
+    splits = lambda **kw: lib.pkv_compress_splits(ctypes.byref(cparams(**kw)))
+    # smallest power of two reaching 1024 workgroups while parts keep >= 16 rows
+    assert splits() == 8                                   # 64 outputs x 8 parts of 16 rows
+    assert splits(num_outputs=1024) == 1
+    assert splits(num_outputs=256, compress_ratio=512) == 4
+    assert splits(num_outputs=16, compress_ratio=512) == 32
+    assert splits(num_outputs=4096, compress_ratio=512) == 2   # a 512-row part touches 65 blocks
+    assert splits(block_size=1, num_outputs=5) == 8            # parts of at most 63 one-row blocks
+    assert splits(num_splits=3) == 3
+    assert splits(num_splits=1, block_size=1) == -4            # 128 blocks in one part
+    assert splits(num_splits=129) == -4
+    assert splits(head_dim=256) == -6
+    assert splits(block_size=0) == -3
+    assert splits(compress_ratio=0) == -2
+    assert splits(num_tokens=0) == -2
+    assert splits(row_stride=1000) == -8
+    assert splits(block_stride=1024) == -8
+    assert splits(max_blocks=1 << 29) == -2                    # max_blocks * B past INT32_MAX
+
+
+def test_compress_workspace_and_argument_checks(lib):
+    p = cparams()
+    assert lib.pkv_compress_workspace_bytes(ctypes.byref(p)) == 2 * 64 * 8 * 512 * 4
+    assert lib.pkv_compress_workspace_bytes(ctypes.byref(cparams(num_outputs=1024))) == 0
+    assert lib.pkv_compress_workspace_bytes(ctypes.byref(cparams(head_dim=7))) == 0
+    fake = ctypes.c_void_p(256)
+    # no outputs: nothing to check, nothing launched
+    assert lib.pkv_compress(ctypes.byref(cparams(num_outputs=0)), None, None, None, None, None,
+                            None, None, 0, None) == 0
+    assert lib.pkv_compress(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, 1 << 20,
+                            None) == -1
+    assert lib.pkv_compress(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, 0,
+                            None) == -5
+    assert lib.pkv_compress(ctypes.byref(p), fake, fake, fake, fake, fake, fake, ctypes.c_void_p(16),
+                            1 << 20, None) == -5                 # workspace not 256-byte aligned

@@ -1,0 +1,193 @@
+"""Paged window compression through the C ABI against the fp64 oracle.
+
+Tolerance, derived from the fp32 arithmetic: the kernel sums at most C
+positive weights and C weighted values sequentially in fp32 (unit roundoff
+u = 2^-24), so the denominator carries a relative error of at most (C - 1) u
+and the numerator an absolute one of at most (C - 1) u * den * max|v|; each
+weight 2^(s log2 e - m) also carries a few ulp from the exponent argument and
+v_exp_f32. Hence per output element |c - ref| <= (2 C u + 4e-6) * max|v| over
+the window's values of that dimension (about 6.5e-5 max|v| at C = 512).
+Addressing is checked bit-exactly: with one finite score per dimension the
+output must equal the selected row's value exactly, and with C = 1 it must
+equal the boundary token's own row.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_36_amd as pkv
+from oracle import compress as oc
+from paged_kv_cache_36_amd import synth
+from tests.parity_util import f64
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected without a GPU")
+    pkv.load()
+
+
+def to_dev(case):
+    for f in ("token_to_req", "positions", "boundaries", "block_table", "state_cache"):
+        setattr(case, f, getattr(case, f).to("cuda"))
+    return case
+
+
+def run(case, num_splits=0):
+    out = pkv.compress(case.state_cache, case.token_to_req, case.positions, case.boundaries,
+                       case.block_table, case.compress_ratio, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def reference(case, outputs=None):
+    """Oracle outputs and per-element bounds for the chosen outputs."""
+    states = f64(case.states)
+    d = case.head_dim
+    bnd = case.boundaries.cpu().numpy()
+    tok = case.token_to_req.cpu().numpy()
+    pos = case.positions.cpu().numpy()
+    per_req = [states[lo:hi] for lo, hi in (case.req_range(r) for r in range(len(case.lens)))]
+    outputs = range(len(bnd)) if outputs is None else outputs
+    ref, bound = {}, {}
+    for j in outputs:
+        r, p = int(tok[bnd[j]]), int(pos[bnd[j]])
+        rows = per_req[r][oc.window_positions(p, case.compress_ratio)]
+        ref[j], _ = oc.compress_window(rows, d)
+        n = rows.shape[0]
+        bound[j] = (2 * n * U + 4e-6) * np.abs(rows[:, :d]).max(axis=0)
+    return ref, bound
+
+
+def check(case, out, outputs=None, what=""):
+    got = f64(out)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    ref, bound = reference(case, outputs)
+    worst = 0.0
+    for j in ref:
+        err = np.abs(got[j] - ref[j])
+        assert np.all(err <= bound[j]), (f"{what}: output {j} err {err.max():.3e} > "
+                                         f"{bound[j][np.argmax(err - bound[j])]:.3e}")
+        worst = max(worst, float((err / bound[j]).max()))
+    return worst
+
+
+SMALL = [
+    # (lens, C, B, boundaries, num_splits)
+    ([1024], 128, 8, "chunk_ends", 0),
+    ([1024], 128, 8, "chunk_ends", 1),
+    ([1024], 128, 8, "chunk_ends", 16),
+    ([700, 650, 651], 64, 8, "all", 0),          # overlapping windows, cut at position 0
+    ([700, 650, 651], 64, 8, "all", 3),          # parts of 22 rows, ragged batches
+    ([3000, 1100], 256, 16, "chunk_ends", 0),
+    ([999, 1001], 100, 5, "all", 0),             # C and B not powers of two
+    ([640], 128, 1, "chunk_ends", 0),            # one row per block: parts capped at 63 rows
+    ([300, 17, 1, 64], 5, 8, "all", 0),
+    ([4096], 512, 8, "chunk_ends", 0),
+    ([4096], 512, 8, "chunk_ends", 2),
+]
+
+
+@pytest.mark.parametrize("lens,c,bsz,bnd,splits", SMALL)
+def test_compress_small_full_check(lens, c, bsz, bnd, splits):
+    print(f"[gpu] compress lens={lens} C={c} B={bsz} boundaries={bnd} S={splits}", flush=True)
+    case = to_dev(synth.build_compress_case("cs", len(lens), sum(lens), c, block_size=bsz,
+                                            seed=sum(lens) + c, lens=lens, boundaries=bnd))
+    out = run(case, splits)
+    check(case, out, what=f"lens={lens} C={c} B={bsz} S={splits}")
+
+
+def test_compress_single_finite_score_is_bit_exact():
+    # the score of (position t, dimension d) stays finite only where
+    # (t + d) % C == 0, so a whole window holds exactly one finite score per
+    # dimension (a window cut at position 0 may hold none): the output must be
+    # that row's value bit for bit (or 0), whatever page holds it
+    print("[gpu] compress one-hot scores", flush=True)
+    lens, c, bsz = [520, 300], 40, 8
+    d = synth.COMPRESS_HEAD
+
+    def one_hot(states, pos):
+        keep = (pos[:, None] + torch.arange(d)[None, :]) % c == 0
+        states[:, d:][~keep] = -float("inf")
+
+    case = synth.build_compress_case("oh", 2, sum(lens), c, block_size=bsz, seed=5, lens=lens,
+                                     boundaries="all", states_fn=one_hot)
+    states = case.states
+    got = run(to_dev(case)).cpu()
+    bnd = case.boundaries.cpu()
+    dims = torch.arange(d)
+    for j in range(bnd.shape[0]):
+        b = int(bnd[j])
+        lo, _ = case.req_range(int(case.token_to_req[b]))
+        p = int(case.positions[b])
+        want = torch.zeros(d)
+        for t in range(max(p - c + 1, 0), p + 1):
+            hit = (t + dims) % c == 0
+            want[hit] = states[lo + t, :d][hit]
+        assert torch.equal(got[j], want), f"output {j} (token {b})"
+
+
+def test_compress_c1_returns_the_row():
+    print("[gpu] compress C=1", flush=True)
+    case = to_dev(synth.build_compress_case("c1", 3, 900, 1, block_size=8, seed=9,
+                                            lens=[400, 250, 250], boundaries="all"))
+    got = run(case).cpu()
+    assert torch.equal(got, case.states[:, :case.head_dim])
+
+
+@pytest.mark.parametrize("name", sorted(synth.COMPRESS_WORKLOADS))
+def test_compress_workloads(name):
+    print(f"[gpu] compress workload {name}", flush=True)
+    case = synth.make_compress_case(name, device="cuda")
+    out = run(case)
+    n = case.num_outputs
+    rng = np.random.default_rng(0)
+    sample = sorted(set([0, 1, n // 2, n - 2, n - 1] + list(rng.integers(0, n, size=11))))
+    check(case, out, outputs=sample if n > 256 else None, what=name)
+
+
+def test_compress_splits_and_block_shuffles():
+    # the same windows in two differently shuffled pools give bitwise equal
+    # outputs for a fixed split; different splits agree within tolerance
+    print("[gpu] compress shuffles and splits", flush=True)
+    kw = dict(block_size=8, lens=[2048, 1536], boundaries="chunk_ends")
+    a = to_dev(synth.build_compress_case("sh", 2, 3584, 256, seed=21, **kw))
+    b = synth.build_compress_case("sh", 2, 3584, 256, seed=21, **kw)
+    # re-lay the same logical rows out through a different block permutation
+    gen = torch.Generator().manual_seed(99)
+    perm = torch.randperm(b.pool_blocks, generator=gen)
+    table = b.block_table.clone()
+    used = table < b.pool_blocks
+    table[used] = perm[table[used].to(torch.int64)].to(torch.int32)
+    cache = torch.full_like(b.state_cache, float("nan"))
+    cache[perm] = b.state_cache[:b.pool_blocks]
+    b.block_table, b.state_cache = table, cache
+    b = to_dev(b)
+    for s in (0, 1, 4, 32):
+        oa, ob = run(a, s), run(b, s)
+        assert torch.equal(oa, ob), s
+        assert torch.equal(oa, run(a, s)), "repeat run differs"
+        check(a, oa, what=f"S={s}")
+
+
+def test_compress_bad_indices_give_nan_rows_and_empty_is_noop():
+    print("[gpu] compress bad indices", flush=True)
+    case = synth.build_compress_case("bad", 2, 600, 64, block_size=8, seed=4, lens=[300, 300],
+                                     boundaries=[63, 127, 599, 700, -1, 200])
+    case.token_to_req[200] = 7          # request past the table
+    case = to_dev(case)
+    for s in (0, 1, 3):
+        out = run(case, s).cpu()
+        assert torch.isnan(out[3:]).all(), s
+        assert torch.isfinite(out[:3]).all(), s
+    empty = to_dev(synth.build_compress_case("e", 1, 64, 64, block_size=8, seed=1,
+                                             boundaries=[]))
+    assert run(empty).shape == (0, 512)
