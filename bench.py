@@ -252,6 +252,57 @@ def measure_prefill(name, steps, warmup, torch, pkv, synth):
     return res
 
 
+def measure_compress(name, steps, warmup, torch, pkv, synth):
+    """Paged window compression of one of the 12 shapes, graph-replayed over
+    cold replicas of the state cache. Algorithmic bytes: every window row read
+    once (4 KiB: 512 fp32 values + 512 fp32 scores) plus the fp32 output."""
+    case = synth.make_compress_case(name, device="cuda")
+    n, c = case.num_outputs, case.compress_ratio
+    rows = sum(min(int(p) + 1, c) for p in case.positions[case.boundaries].tolist())
+    nbytes = rows * 2 * case.head_dim * 4 + n * case.head_dim * 4
+    copies = max(1, math.ceil(COLD_BYTES / nbytes))
+    caches = [case.state_cache] + [case.state_cache.clone() for _ in range(copies - 1)]
+    prm = pkv.compress_params(case.state_cache, case.token_to_req, case.boundaries,
+                              case.block_table, c)
+    splits = pkv.compress_splits(prm)
+    out = torch.empty((n, case.head_dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.compress_workspace_bytes(prm), 256), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        pkv.compress(caches[i % copies], case.token_to_req, case.positions, case.boundaries,
+                     case.block_table, c, out=out, workspace=ws)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    gbps = nbytes / (us * 1e-6) / 1e9
+    res = {"workload": name, "kernel": "compress_split_kernel" + ("+compress_combine_kernel"
+                                                                 if splits > 1 else ""),
+           "num_outputs": n, "compress_ratio": c, "tokens": int(case.positions.shape[0]),
+           "num_splits": splits, "workgroups": n * splits, "cold_copies": copies,
+           "steps": steps, "algorithmic_bytes": nbytes, "us_per_call": round(us, 3),
+           "gbps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
+    log(json.dumps(res))
+    del g, caches, case, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_probe(torch, pkv, reps=20):
     buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
@@ -399,7 +450,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", default="all",
-                    help="main, all, or one workload name (timed alone, reported as extra)")
+                    help="main, all, prefill, compress, or one workload name (timed alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also launch the plain copy kernel (counter calibration runs)")
@@ -424,17 +475,20 @@ def main():
     if args.copy_probe:
         copy_probe(torch, pkv)
 
-    if args.workloads not in ("main", "all", "prefill"):
+    if args.workloads not in ("main", "all", "prefill", "compress"):
         name = args.workloads
         if name in synth.WORKLOADS:
             res = measure(name, args.steps, args.warmup, torch, pkv, synth)
         elif name in synth.PREFILL_WORKLOADS:
             res = measure_prefill(name, args.steps, args.warmup, torch, pkv, synth)
+        elif name in synth.COMPRESS_WORKLOADS:
+            res = measure_compress(name, args.steps, args.warmup, torch, pkv, synth)
         elif name in APPEND_WORKLOADS:
             res = measure_append(name, *APPEND_WORKLOADS[name], args.steps, args.warmup,
                                  torch, pkv, synth)
         else:
-            known = sorted(synth.WORKLOADS) + sorted(synth.PREFILL_WORKLOADS) + sorted(APPEND_WORKLOADS)
+            known = (sorted(synth.WORKLOADS) + sorted(synth.PREFILL_WORKLOADS) +
+                     sorted(APPEND_WORKLOADS) + sorted(synth.COMPRESS_WORKLOADS))
             sys.exit(f"unknown workload {name}; choose from {known}")
         print(json.dumps({"workload_only": res}), flush=True)
         return
@@ -457,6 +511,11 @@ def main():
         for name in sorted(synth.PREFILL_WORKLOADS):
             prefills.append(measure_prefill(name, min(args.steps, 20), min(args.warmup, 3),
                                             torch, pkv, synth))
+    compresses = []
+    if args.workloads in ("all", "compress"):
+        for name in sorted(synth.COMPRESS_WORKLOADS, key=lambda w: synth.COMPRESS_WORKLOADS[w]):
+            compresses.append(measure_compress(name, min(args.steps, 100), args.warmup, torch,
+                                               pkv, synth))
     probe = read_probe(torch, pkv)
     log(f"read probe (2 GiB streaming read): {probe} GB/s")
 
@@ -504,6 +563,7 @@ def main():
         "workloads": [main_res] + extra,
         "append": appends,
         "prefill": prefills,
+        "compress": compresses,
     }
     print(json.dumps(line), flush=True)
 

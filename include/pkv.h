@@ -318,8 +318,8 @@ typedef struct {
   int32_t block_size;      /* B state rows per block, > 0 (8 on the page)          */
   int32_t compress_ratio;  /* C window length, >= 1 (128, 256, 512 on the page)    */
   int32_t num_splits;      /* 0: the library chooses; else S window parts per
-                              output, 1 <= S <= C, each touching at most 64 blocks
-                              (ceil((ceil(C/S) - 1) / B) + 1 <= 64)                */
+                              output, 1 <= S <= min(C, 64), each touching at most
+                              64 blocks (ceil((ceil(C/S) - 1) / B) + 1 <= 64)      */
   int64_t block_stride;    /* elements between state blocks (>= B * row_stride)    */
   int64_t row_stride;      /* elements between rows of a block (>= 2 D), multiple
                               of 4                                                 */

@@ -17,6 +17,7 @@ from .api import (  # noqa: F401
     compress,
     compress_params,
     compress_splits,
+    compress_workspace_bytes,
     debug_gather,
     debug_resolve,
     decode,

@@ -308,6 +308,10 @@ def compress_splits(p) -> int:
     return int(load().pkv_compress_splits(ctypes.byref(p)))
 
 
+def compress_workspace_bytes(p) -> int:
+    return int(load().pkv_compress_workspace_bytes(ctypes.byref(p)))
+
+
 def compress(state_cache, token_to_req, positions, boundary_token_indices, block_table,
              compress_ratio, *, num_splits=0, out=None, workspace=None, stream=None):
     """Per-dimension softmax compression of each boundary token's window of

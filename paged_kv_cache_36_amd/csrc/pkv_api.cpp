@@ -515,7 +515,8 @@ namespace {
 // Window parts per output: the caller's S, else the smallest power of two that
 // gives at least 1024 workgroups while parts keep 16 rows or more. Every part
 // must touch at most kCompressMaxBlocks logical blocks (its ids sit one per
-// lane). Returns a negative status for invalid params.
+// lane), and an output has at most kCompressMaxSplits parts (the combine's
+// lanes). Returns a negative status for invalid params.
 int32_t compress_splits(const pkv_compress_params* p) {
   if (!p) return PKV_ERR_NULL;
   if (p->head_dim != pkv::kCompressDim) return PKV_ERR_UNSUPPORTED;
@@ -534,7 +535,7 @@ int32_t compress_splits(const pkv_compress_params* p) {
     return (rows - 1 + p->block_size - 1) / p->block_size + 1;
   };
   int64_t s = p->num_splits;
-  if (s < 0 || s > c) return PKV_ERR_PARTITION;
+  if (s < 0 || s > c || s > pkv::kCompressMaxSplits) return PKV_ERR_PARTITION;
   if (s > 0) {
     if (blocks_touched(s) > pkv::kCompressMaxBlocks) return PKV_ERR_PARTITION;
   } else {
@@ -543,6 +544,7 @@ int32_t compress_splits(const pkv_compress_params* p) {
     while (static_cast<int64_t>(p->num_outputs) * s < 1024 && (c + 2 * s - 1) / (2 * s) >= 16)
       s *= 2;
     if (s > c) s = c;
+    if (s > pkv::kCompressMaxSplits) return PKV_ERR_UNSUPPORTED;
   }
   if (static_cast<int64_t>(p->num_outputs) * s > INT32_MAX) return PKV_ERR_SHAPE;
   return static_cast<int32_t>(s);
@@ -597,6 +599,8 @@ pkv_status pkv_compress(const pkv_compress_params* p, const float* state_cache,
   a.compress_ratio = p->compress_ratio;
   a.num_splits = s;
   a.part_rows = (p->compress_ratio + s - 1) / s;
+  a.combine_lanes = 1;
+  while (a.combine_lanes * 8 < s) a.combine_lanes *= 2;
   return hip_status(pkv::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 

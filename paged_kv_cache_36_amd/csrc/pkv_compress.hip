@@ -218,33 +218,83 @@ __global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArg
   }
 }
 
-// One thread per (output, dimension): c = sum_p 2^(lse_p - LSE) c_p with the
-// maximum taken first. An output whose parts all carry lse = +inf (bad
-// indices) comes out NaN; one with no finite score comes out 0.
-__global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressArgs a) {
-  const int per_out = kCompressDim / kCmpThreads;
-  const int n = blockIdx.x / per_out;
-  const int dim = (blockIdx.x - n * per_out) * kCmpThreads + threadIdx.x;
-  const int64_t base = static_cast<int64_t>(n) * a.num_splits * kCompressDim + dim;
-  float mt = -INFINITY;
-  for (int j = 0; j < a.num_splits; ++j) mt = fmaxf(mt, a.lse_part[base + j * kCompressDim]);
-  float c = 0.f;
-  if (mt != -INFINITY) {
-    float tot = 0.f, acc = 0.f;
-    for (int j = 0; j < a.num_splits; ++j) {
-      const float l = a.lse_part[base + j * kCompressDim];
-      const float o = a.o_part[base + j * kCompressDim];
-      const float wgt = exp2_fast(l - mt);
-      if (wgt > 0.f) {   // parts without rows carry c = 0 and weight 0
-        tot += wgt;
-        acc = __builtin_fmaf(wgt, o, acc);
-      } else if (wgt != wgt) {
-        tot = __builtin_nanf("");
-      }
-    }
-    c = acc / tot;
+// Merge of several (m, weight sum, weighted sum) states of one dimension:
+// m is a log2-sum-exp reference; an m of +inf (bad indices) poisons the
+// result with NaN, an m of -inf (no finite score) carries no weight.
+struct CmbState {
+  f32x4 m, tot, acc;
+};
+
+__device__ __forceinline__ void cmb_merge(CmbState& x, const f32x4& m2, const f32x4& t2,
+                                          const f32x4& a2) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float mt = fmaxf(x.m[d], m2[d]);
+    const float mref = mt == -INFINITY ? 0.f : mt;
+    const float w1 = exp2_fast(x.m[d] - mref);
+    const float w2 = exp2_fast(m2[d] - mref);
+    x.tot[d] = x.tot[d] * w1 + t2[d] * w2;
+    x.acc[d] = x.acc[d] * w1 + a2[d] * w2;
+    x.m[d] = mt;
   }
-  a.out[static_cast<int64_t>(n) * kCompressDim + dim] = c;
+}
+
+__device__ __forceinline__ f32x4 shfl_xor4(const f32x4& v, int mask) {
+  return f32x4{__shfl_xor(v[0], mask), __shfl_xor(v[1], mask), __shfl_xor(v[2], mask),
+               __shfl_xor(v[3], mask)};
+}
+
+// G = a.combine_lanes (a power of two, S <= 8 G) adjacent lanes share one
+// (output, 4-dimension group); lane g of them merges parts 8 g .. 8 g + 7, all
+// its loads in flight at once, and the G lanes then merge with xor shuffles:
+// c = sum_p 2^(lse_p - LSE) c_p / sum_p 2^(lse_p - LSE).
+constexpr int kCmbPartsPerLane = 8;
+
+__global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressArgs a) {
+  const int g_lanes = a.combine_lanes;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCmpThreads + threadIdx.x;
+  const int64_t group = t / g_lanes;                  // (output, 4-dim group)
+  const int pg = static_cast<int>(t - group * g_lanes);
+  const int groups_per_out = kCompressDim / 4;
+  const bool live = group < static_cast<int64_t>(a.num_outputs) * groups_per_out;
+  const int64_t n = live ? group / groups_per_out : 0;
+  const int dim = static_cast<int>(group - n * groups_per_out) * 4;
+  const int64_t base = n * a.num_splits * kCompressDim + dim;
+  f32x4 l[kCmbPartsPerLane], o[kCmbPartsPerLane];
+#pragma unroll
+  for (int i = 0; i < kCmbPartsPerLane; ++i) {
+    const int j = pg * kCmbPartsPerLane + i;
+    l[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (live && j < a.num_splits) {
+      l[i] = *reinterpret_cast<const f32x4*>(a.lse_part + base + static_cast<int64_t>(j) * kCompressDim);
+      o[i] = *reinterpret_cast<const f32x4*>(a.o_part + base + static_cast<int64_t>(j) * kCompressDim);
+    }
+  }
+  CmbState x;
+  x.m = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  x.tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  x.acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kCmbPartsPerLane; ++i) {
+    // a part holds c_p with weight 2^(lse_p - lse_p) = 1; an empty part
+    // (lse_p = -inf) holds c_p = 0 and no weight
+    f32x4 w = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (l[i][d] == -INFINITY) w[d] = 0.f;
+    cmb_merge(x, l[i], w, o[i] * w);
+  }
+  for (int mask = 1; mask < g_lanes; mask <<= 1)   // uniform trip count
+    cmb_merge(x, shfl_xor4(x.m, mask), shfl_xor4(x.tot, mask), shfl_xor4(x.acc, mask));
+  if (!live || pg != 0) return;
+  f32x4 c;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    c[d] = x.tot[d] > 0.f ? x.acc[d] / x.tot[d] : 0.f;
+    if (x.tot[d] != x.tot[d] || x.m[d] == INFINITY) c[d] = __builtin_nanf("");
+  }
+  *reinterpret_cast<f32x4*>(a.out + n * kCompressDim + dim) = c;
 }
 
 }  // namespace
@@ -256,7 +306,8 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
                      dim3(kCmpThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  const int64_t cblocks = static_cast<int64_t>(a.num_outputs) * (kCompressDim / kCmpThreads);
+  const int64_t threads = static_cast<int64_t>(a.num_outputs) * (kCompressDim / 4) * a.combine_lanes;
+  const int64_t cblocks = (threads + kCmpThreads - 1) / kCmpThreads;
   hipLaunchKernelGGL(compress_combine_kernel, dim3(static_cast<uint32_t>(cblocks)),
                      dim3(kCmpThreads), 0, stream, a);
   return hipGetLastError();

@@ -86,6 +86,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // window of state rows [values(D) | scores(D)], fp32, D = kCompressDim.
 constexpr int kCompressDim = 512;
 constexpr int kCompressMaxBlocks = 64;   // logical blocks one window part may touch
+constexpr int kCompressMaxSplits = 64;   // window parts per output the combine merges
 struct CompressArgs {
   const float* state;             // paged state cache
   const int32_t* token_to_req;    // [num_tokens]
@@ -105,6 +106,7 @@ struct CompressArgs {
   int32_t compress_ratio;
   int32_t num_splits;             // window parts per output
   int32_t part_rows;              // ceil(compress_ratio / num_splits)
+  int32_t combine_lanes;          // lanes per (output, 4 dims) in the combine: 1, 2, 4 or 8
 };
 // split kernel, then (num_splits > 1) the combine kernel
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);

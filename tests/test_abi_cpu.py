@@ -277,6 +277,8 @@ def test_compress_splits_auto_and_limits(lib):
     assert splits(num_splits=3) == 3
     assert splits(num_splits=1, block_size=1) == -4            # 128 blocks in one part
     assert splits(num_splits=129) == -4
+    assert splits(num_splits=65, compress_ratio=512) == -4     # the combine merges 64 parts
+    assert splits(block_size=1, compress_ratio=5000) == -6     # would need 79 parts
     assert splits(head_dim=256) == -6
     assert splits(block_size=0) == -3
     assert splits(compress_ratio=0) == -2
