@@ -303,9 +303,8 @@ PKV_API pkv_status pkv_prefill(const pkv_prefill_params* params, const void* q,
  * state row o = t % B of block block_table[r, t / B]; its first D = 512 floats
  * are values v_t and the next 512 scores s_t. The output, per dimension d:
  *   compressed[n, d] = sum_t softmax_t(s_{t,d}) v_{t,d}   (over the window).
- * A dimension whose window scores are all -inf gives 0. Only this reduction
- * stage is built; RMSNorm, INT8 quantisation, RoPE and the byte scatter of
- * the page's finalizer are not.
+ * A dimension whose window scores are all -inf gives 0. The page's finalizer
+ * (RMSNorm, INT8 quantisation, RoPE, byte scatter) is pkv_compress_finalize.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t num_outputs;     /* N boundary tokens (0 is a no-op)                     */
@@ -348,6 +347,50 @@ PKV_API pkv_status pkv_compress(const pkv_compress_params* params, const float* 
                                 const int64_t* boundary_token_indices, const int32_t* block_table,
                                 float* compressed, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* The compression finalizer ("From Attention to KV Cache Compression: Notes
+ * from a KernelGen Optimization", "How One Output Is Produced" and "The
+ * Finalizer's Sharp Edges"), applied to pkv_compress's output. For output n
+ * with boundary token b, position p = positions[b] and slot =
+ * kv_slot_mapping[b]:
+ *   y = c * rho * w with rho = (mean(c^2) + eps)^-1/2     (fp32)
+ *   dims 0..447: z = bf16(y) read back as fp32; per group g of 64 dims,
+ *     a = max(max|z|, 1e-4), e = ceil(log2(a * (1/127))) (exact for the fp32
+ *     product), code q = trunc(z * 2^-e) clipped to [-127, 127]
+ *   dims 448..511: GPT-J pairs (y[448+2j], y[449+2j]) rotated by cos_j =
+ *     cos_sin_cache[pc, j], sin_j = cos_sin_cache[pc, 32 + j], pc = (p / C) * C,
+ *     rounded to bf16
+ *   KV page slot / 64, slot offset o = slot % 64: bytes o*576 .. +575 get
+ *   [448 int8 codes][64 bf16], bytes 64*576 + o*8 .. +7 get [7 x (e + 127)][0].
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t num_outputs;     /* N (0 is a no-op)                                      */
+  int32_t num_tokens;      /* T entries of positions and kv_slot_mapping (>= 1 when
+                              N > 0)                                                */
+  int32_t compress_ratio;  /* C >= 1                                                */
+  int32_t cos_sin_rows;    /* rows of cos_sin_cache                                 */
+  int64_t num_kv_pages;    /* pages of kv_cache                                     */
+  int64_t kv_page_stride;  /* bytes between KV pages: >= 64 * 584, multiple of 16   */
+  float rms_norm_eps;      /* eps >= 0, finite (1e-6 on the page)                   */
+} pkv_finalize_params;
+
+/* Device inputs: compressed fp32 [N, 512]; positions and kv_slot_mapping int64
+ * [T]; boundary_token_indices int64 [N]; rms_norm_weight fp32 [512];
+ * cos_sin_cache fp32 [cos_sin_rows, 64]. Device output: kv_cache bytes
+ * [num_kv_pages, kv_page_stride]; only the written slots' 576 + 8 bytes
+ * change. An output whose boundary index is outside [0, T), whose slot is
+ * negative or past the cache, whose position is negative or whose RoPE row is
+ * past cos_sin_cache writes nothing; non-finite compressed values give
+ * unspecified bytes. Two outputs aimed at one slot leave either's bytes.
+ * 16-byte aligned float and byte pointers, 8-byte aligned index pointers.
+ * Asynchronous on `stream`; allocates nothing; host checks return an error
+ * before any launch. */
+PKV_API pkv_status pkv_compress_finalize(const pkv_finalize_params* params,
+                                         const float* compressed, const int64_t* positions,
+                                         const int64_t* boundary_token_indices,
+                                         const float* rms_norm_weight, const float* cos_sin_cache,
+                                         const int64_t* kv_slot_mapping, void* kv_cache,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

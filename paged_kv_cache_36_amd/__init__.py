@@ -4,7 +4,8 @@ The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
 ``paged_kv_cache_36_amd.api`` is its thin Python binding. Besides decode, the
 library writes new tokens into the paged cache (``append``), runs the causal
 tail-Q prefill of one sequence (``prefill``), compresses windows of a paged
-state cache (``compress``) and computes the page-size rule (``page_tokens``).
+state cache and packs the results into KV pages (``compress``,
+``compress_finalize``) and computes the page-size rule (``page_tokens``).
 ``synth`` draws the seeded synthetic inputs.
 """
 
@@ -14,7 +15,9 @@ from .api import (  # noqa: F401
     append,
     combine,
     combine_balanced,
+    KV_PAGE_BYTES,
     compress,
+    compress_finalize,
     compress_params,
     compress_splits,
     compress_workspace_bytes,

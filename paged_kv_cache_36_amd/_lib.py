@@ -90,6 +90,18 @@ class CompressParams(ctypes.Structure):
     ]
 
 
+class FinalizeParams(ctypes.Structure):
+    _fields_ = [
+        ("num_outputs", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("compress_ratio", ctypes.c_int32),
+        ("cos_sin_rows", ctypes.c_int32),
+        ("num_kv_pages", ctypes.c_int64),
+        ("kv_page_stride", ctypes.c_int64),
+        ("rms_norm_eps", ctypes.c_float),
+    ]
+
+
 _P = ctypes.POINTER(DecodeParams)
 _VP = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -116,6 +128,8 @@ SIGNATURES = {
     "pkv_compress_workspace_bytes": (_SZ, [ctypes.POINTER(CompressParams)]),
     "pkv_compress": (_I32, [ctypes.POINTER(CompressParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                             _SZ, _VP]),
+    "pkv_compress_finalize": (_I32, [ctypes.POINTER(FinalizeParams), _VP, _VP, _VP, _VP, _VP, _VP,
+                                     _VP, _VP]),
     "pkv_probe_sink_floats": (_I32, []),
     "pkv_probe_read": (_I32, [_VP, _SZ, _VP, _VP]),
     "pkv_probe_copy": (_I32, [_VP, _VP, _SZ, _VP]),

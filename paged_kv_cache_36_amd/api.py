@@ -13,7 +13,8 @@ import ctypes
 
 import torch
 
-from ._lib import AppendParams, CompressParams, DecodeParams, PlanInfo, PrefillParams, load
+from ._lib import (AppendParams, CompressParams, DecodeParams, FinalizeParams, PlanInfo,
+                   PrefillParams, load)
 
 HEAD_SIZE = 256
 GROUP = 6
@@ -342,6 +343,48 @@ def compress(state_cache, token_to_req, positions, boundary_token_indices, block
                                0 if workspace is None else workspace.numel(), _stream(stream)),
            "pkv_compress")
     return out
+
+
+KV_PAGE_BYTES = 64 * (576 + 8)   # one packed KV page: 64 slots of payload, then their scales
+
+
+def compress_finalize(compressed, positions, boundary_token_indices, rms_norm_weight,
+                      cos_sin_cache, kv_slot_mapping, kv_cache, compress_ratio,
+                      rms_norm_eps=1.0e-6, stream=None):
+    """Write each output's packed bytes (INT8 NOPE codes, bf16 RoPE, scale
+    bytes) into kv_cache (uint8 [pages, page_bytes], rows contiguous)."""
+    _need(compressed, "compressed", torch.float32, 2)
+    _need(positions, "positions", torch.int64, 1)
+    _need(boundary_token_indices, "boundary_token_indices", torch.int64, 1)
+    _need(rms_norm_weight, "rms_norm_weight", torch.float32, 1)
+    _need(cos_sin_cache, "cos_sin_cache", torch.float32, 2)
+    _need(kv_slot_mapping, "kv_slot_mapping", torch.int64, 1)
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    for t, name in ((compressed, "compressed"), (positions, "positions"),
+                    (boundary_token_indices, "boundary_token_indices"),
+                    (rms_norm_weight, "rms_norm_weight"), (cos_sin_cache, "cos_sin_cache"),
+                    (kv_slot_mapping, "kv_slot_mapping")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if kv_cache.stride(1) != 1:
+        raise ValueError("kv_cache pages must be contiguous bytes")
+    if compressed.shape[1] != 512 or rms_norm_weight.shape[0] != 512 or cos_sin_cache.shape[1] != 64:
+        raise ValueError("compressed [N, 512], rms_norm_weight [512], cos_sin_cache [rows, 64]")
+    if kv_slot_mapping.shape[0] != positions.shape[0]:
+        raise ValueError("kv_slot_mapping and positions differ in length")
+    p = FinalizeParams()
+    p.num_outputs = compressed.shape[0]
+    p.num_tokens = positions.shape[0]
+    p.compress_ratio = int(compress_ratio)
+    p.cos_sin_rows = cos_sin_cache.shape[0]
+    p.num_kv_pages = kv_cache.shape[0]
+    p.kv_page_stride = kv_cache.stride(0)
+    p.rms_norm_eps = float(rms_norm_eps)
+    _check(load().pkv_compress_finalize(ctypes.byref(p), _ptr(compressed), _ptr(positions),
+                                        _ptr(boundary_token_indices), _ptr(rms_norm_weight),
+                                        _ptr(cos_sin_cache), _ptr(kv_slot_mapping), _ptr(kv_cache),
+                                        _stream(stream)), "pkv_compress_finalize")
+    return kv_cache
 
 
 def page_tokens(state_page_bytes: int, attn_bytes_per_token: int, alignment_tokens: int) -> int:

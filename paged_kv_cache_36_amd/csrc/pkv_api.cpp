@@ -604,6 +604,44 @@ pkv_status pkv_compress(const pkv_compress_params* p, const float* state_cache,
   return hip_status(pkv::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_compress_finalize(const pkv_finalize_params* p, const float* compressed,
+                                 const int64_t* positions, const int64_t* boundary_token_indices,
+                                 const float* rms_norm_weight, const float* cos_sin_cache,
+                                 const int64_t* kv_slot_mapping, void* kv_cache, void* stream) {
+  if (!p) return PKV_ERR_NULL;
+  if (p->num_outputs < 0 || p->num_tokens < 0 || p->compress_ratio < 1 || p->cos_sin_rows < 0 ||
+      p->num_kv_pages < 0 || (p->num_outputs > 0 && p->num_tokens < 1) ||
+      !std::isfinite(p->rms_norm_eps) || p->rms_norm_eps < 0.f ||
+      p->num_kv_pages > INT64_MAX / (pkv::kKvBlockSize * 2))
+    return PKV_ERR_SHAPE;
+  if (p->kv_page_stride < pkv::kKvBlockSize * (pkv::kKvTokenStride + pkv::kKvScaleDim) ||
+      p->kv_page_stride % 16 != 0)
+    return PKV_ERR_STRIDE;
+  if (p->num_outputs == 0) return PKV_OK;
+  if (!compressed || !positions || !boundary_token_indices || !rms_norm_weight ||
+      !cos_sin_cache || !kv_slot_mapping || !kv_cache || !aligned(compressed, 16) ||
+      !aligned(rms_norm_weight, 16) || !aligned(cos_sin_cache, 16) || !aligned(kv_cache, 16) ||
+      !aligned(positions, 8) || !aligned(boundary_token_indices, 8) ||
+      !aligned(kv_slot_mapping, 8))
+    return PKV_ERR_NULL;
+  pkv::FinalizeArgs a;
+  a.compressed = compressed;
+  a.positions = positions;
+  a.boundaries = boundary_token_indices;
+  a.weight = rms_norm_weight;
+  a.cos_sin = cos_sin_cache;
+  a.slots = kv_slot_mapping;
+  a.kv = static_cast<uint8_t*>(kv_cache);
+  a.num_kv_pages = p->num_kv_pages;
+  a.kv_page_stride = p->kv_page_stride;
+  a.num_outputs = p->num_outputs;
+  a.num_tokens = p->num_tokens;
+  a.compress_ratio = p->compress_ratio;
+  a.cos_sin_rows = p->cos_sin_rows;
+  a.eps = p->rms_norm_eps;
+  return hip_status(pkv::launch_finalize(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,
                         int32_t alignment_tokens) {
   if (state_page_bytes <= 0 || attn_bytes_per_token <= 0 || alignment_tokens <= 0) return -1;

@@ -297,6 +297,127 @@ __global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressA
   *reinterpret_cast<f32x4*>(a.out + n * kCompressDim + dim) = c;
 }
 
+// ---------------------------------------------------------------------------
+// Finalizer ("From Attention to KV Cache Compression: Notes from a KernelGen
+// Optimization", "How One Output Is Produced" and "The Finalizer's Sharp
+// Edges"). One wave per output; lane l holds dims 8 l .. 8 l + 7.
+//  - rho = (mean c^2 + eps)^-1/2 (wave sum), y = (c rho) w;
+//  - lanes 0..55 (dims 0..447): z = bf16(y) round trip; group g of 64 dims =
+//    lanes 8 g .. 8 g + 7: a = max(max |z|, 1e-4), e = ceil(log2 fl32(a *
+//    fl32(1/127))) taken exactly from the fp32 exponent and mantissa,
+//    q = trunc(z 2^-e) clipped to [-127, 127], stored as a byte;
+//  - lanes 56..63 (dims 448..511): GPT-J pairs (y[448 + 2j], y[449 + 2j])
+//    rotated by row (p / C) * C of cos_sin (cos j, sin 32 + j), stored bf16;
+//  - the slot's page gets payload [448 INT8][64 bf16] at (slot % 64) * 576
+//    and scale bytes [7 x (e + 127)][0] at 64 * 576 + (slot % 64) * 8.
+// An output whose boundary index, slot or RoPE row is out of range writes
+// nothing.
+// ---------------------------------------------------------------------------
+constexpr int kFinThreads = 256;
+constexpr int kNopeLanes = 56;   // 448 dims / 8
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(FinalizeArgs a) {
+  const int lane = lane_id();
+  const int n = blockIdx.x * (kFinThreads / 64) + wave_id();
+  if (n >= a.num_outputs) return;
+  const int64_t b = a.boundaries[n];
+  if (b < 0 || b >= a.num_tokens) return;
+  const int64_t slot = a.slots[b];
+  const int64_t p = a.positions[b];
+  if (slot < 0 || slot >= a.num_kv_pages * kKvBlockSize || p < 0) return;
+  const int64_t pc = (p / a.compress_ratio) * a.compress_ratio;
+  if (pc >= a.cos_sin_rows) return;
+
+  const float* crow = a.compressed + static_cast<int64_t>(n) * kCompressDim + 8 * lane;
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(crow);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(crow + 4);
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane + 4);
+  float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sq = __builtin_fmaf(c[i], c[i], sq);
+  const float mean = wave_sum(sq) * (1.f / kCompressDim);
+  const float rho = __builtin_amdgcn_rsqf(mean + a.eps);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (c[i] * rho) * w[i];
+
+  uint8_t* page = a.kv + (slot / kKvBlockSize) * a.kv_page_stride;
+  const int off = static_cast<int>(slot % kKvBlockSize);
+  uint8_t* payload = page + off * kKvTokenStride;
+
+  // NOPE: the group max is taken over all lanes (RoPE lanes join with 0 and
+  // their own group result is unused)
+  float z[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    z[i] = __uint_as_float(bf16_bits(y[i]) << 16);
+    amax = fmaxf(amax, fabsf(z[i]));
+  }
+  if (lane >= kNopeLanes) amax = 0.f;
+#pragma unroll
+  for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float av = fmaxf(amax, 1.0e-4f);
+  const float yq = av * (1.0f / 127.0f);
+  int ex;
+  const float mant = frexpf(yq, &ex);
+  const int e = mant == 0.5f ? ex - 1 : ex;
+  if (lane < kNopeLanes) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = truncf(ldexpf(z[i], -e));
+      q = fminf(fmaxf(q, -127.f), 127.f);
+      const uint32_t byte = static_cast<uint32_t>(static_cast<int>(q)) & 0xffu;
+      if (i < 4) lo |= byte << (8 * i);
+      else hi |= byte << (8 * (i - 4));
+    }
+    *reinterpret_cast<u32x2*>(payload + 8 * lane) = u32x2{lo, hi};
+  } else {
+    // pairs j = 4 (lane - 56) + k: (u, w) = (y[2k], y[2k + 1])
+    const int j0 = 4 * (lane - kNopeLanes);
+    const float* row = a.cos_sin + pc * 64;
+    const f32x4 cs = *reinterpret_cast<const f32x4*>(row + j0);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(row + 32 + j0);
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float u = y[2 * k], v = y[2 * k + 1];
+      const float ru = u * cs[k] - v * sn[k];
+      const float rv = v * cs[k] + u * sn[k];
+      packed[k] = bf16_bits(ru) | (bf16_bits(rv) << 16);
+    }
+    *reinterpret_cast<u32x4*>(payload + 8 * kNopeLanes + 16 * (lane - kNopeLanes)) =
+        u32x4{packed[0], packed[1], packed[2], packed[3]};
+  }
+  // scale bytes: exponent of group g sits in lane 8 g
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int g = 0; g < 7; ++g) {
+    const uint32_t byte = static_cast<uint32_t>(__shfl(e, 8 * g) + 127) & 0xffu;
+    if (g < 4) lo |= byte << (8 * g);
+    else hi |= byte << (8 * (g - 4));
+  }
+  if (lane == 0)
+    *reinterpret_cast<u32x2*>(page + kKvBlockSize * kKvTokenStride + off * kKvScaleDim) =
+        u32x2{lo, hi};
+}
+
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
@@ -310,6 +431,15 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   const int64_t cblocks = (threads + kCmpThreads - 1) / kCmpThreads;
   hipLaunchKernelGGL(compress_combine_kernel, dim3(static_cast<uint32_t>(cblocks)),
                      dim3(kCmpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t stream) {
+  if (a.num_outputs <= 0) return hipSuccess;
+  const int per_block = kFinThreads / 64;
+  const int64_t blocks = (static_cast<int64_t>(a.num_outputs) + per_block - 1) / per_block;
+  hipLaunchKernelGGL(finalize_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kFinThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -110,6 +110,28 @@ struct CompressArgs {
 };
 // split kernel, then (num_splits > 1) the combine kernel
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+// The compression finalizer: RMSNorm, NOPE INT8 + scale bytes, GPT-J RoPE in
+// bf16, written into 64-slot KV pages of 64 * (576 + 8) bytes.
+constexpr int kKvBlockSize = 64;
+constexpr int kKvTokenStride = 576;
+constexpr int kKvScaleDim = 8;
+struct FinalizeArgs {
+  const float* compressed;        // [num_outputs, 512]
+  const int64_t* positions;       // [num_tokens]
+  const int64_t* boundaries;      // [num_outputs]
+  const float* weight;            // [512]
+  const float* cos_sin;           // [cos_sin_rows, 64]: cos 0..31, sin 32..63
+  const int64_t* slots;           // [num_tokens]
+  uint8_t* kv;                    // [num_kv_pages, kv_page_stride bytes]
+  int64_t num_kv_pages;
+  int64_t kv_page_stride;
+  int32_t num_outputs;
+  int32_t num_tokens;
+  int32_t compress_ratio;
+  int32_t cos_sin_rows;
+  float eps;
+};
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t stream);
 int32_t probe_sink_floats();
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

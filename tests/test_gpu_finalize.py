@@ -1,0 +1,210 @@
+"""The compression finalizer through the C ABI against the fp64 oracle.
+
+Bytes are compared exactly, with one allowance the arithmetic forces. The
+pages form y = c rho w in fp32 with an unspecified summation order; the
+kernel's y is within 16 u |y| of the exact value (u = 2^-24: the sum of 512
+squares over a wave, the reciprocal square root, two products), so where the
+exact y lies within that band of a bf16 rounding tie, either bf16 neighbour is
+a correct round trip, and the int8 code (and, if it is the group's maximum, the
+group exponent) may follow either. A RoPE output carries an absolute error of
+up to 16 u (|u cos| + |w sin|), which spans several bf16 steps where the sum
+cancels; any bf16 value within that band is accepted there. The test allows
+32 u, accepts exactly the values inside the band, and requires departures
+from the nearest value to stay rare (they are counted). Everything
+else (exponent bytes, codes, bf16 bits, the pad byte, slot placement, bytes
+left untouched) must match bit for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_36_amd as pkv
+from oracle import compress as oc
+from oracle import decode as od
+from paged_kv_cache_36_amd import synth
+from tests.parity_util import f64
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+BAND = 32 * U
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected without a GPU")
+    pkv.load()
+
+
+def bf16_neighbours(x, band):
+    """bf16 values a correct fp32 round trip of x may give: the nearest, and
+    the range [lo, hi] of every bf16 value within band of x (where a sum
+    cancels, the band can span several bf16 steps)."""
+    near = oc.bf16_round(x)
+    lo = oc.bf16_round(x - band)
+    hi = oc.bf16_round(x + band)
+    return near, lo, hi
+
+
+def rope_table(rows, seed):
+    g = torch.Generator().manual_seed(seed)
+    pos = torch.arange(rows, dtype=torch.float64)[:, None]
+    inv = 10000.0 ** (-torch.arange(32, dtype=torch.float64) * 2 / 64)
+    th = pos * inv[None, :] + torch.rand((1, 32), generator=g, dtype=torch.float64)
+    return torch.cat([torch.cos(th), torch.sin(th)], 1).to(torch.float32)
+
+
+def check_output(got_payload, got_scale, c, weight, eps, cs_row):
+    """Returns the number of elements that took the other admissible value."""
+    y = oc.rms_norm(c, weight, eps)
+    alt = 0
+    # NOPE
+    yn = y[:448]
+    near, lo, hi = bf16_neighbours(yn, BAND * np.abs(yn))
+    codes = got_payload[:448].astype(np.int64)
+    codes = np.where(codes > 127, codes - 256, codes)
+    e_got = got_scale[:7].astype(np.int64) - 127
+    assert got_scale[7] == 0
+    for g in range(7):
+        sl = slice(64 * g, 64 * g + 64)
+        amax_lo = np.max(np.minimum(np.abs(lo[sl]), np.abs(hi[sl])))
+        amax_hi = np.max(np.maximum(np.abs(lo[sl]), np.abs(hi[sl])))
+        e_near = oc.quant_exponent(np.abs(near[sl]).max())
+        e_ok = {oc.quant_exponent(amax_lo), oc.quant_exponent(amax_hi), e_near}
+        assert e_got[g] in e_ok, (g, e_got[g], e_ok)
+        alt += int(e_got[g] != e_near)
+        step = 2.0 ** (-int(e_got[g]))
+        want = np.clip(np.trunc(near[sl] * step), -127, 127)
+        q_lo = np.clip(np.trunc(lo[sl] * step), -127, 127)   # trunc and clip are monotone
+        q_hi = np.clip(np.trunc(hi[sl] * step), -127, 127)
+        ok = (codes[sl] >= q_lo) & (codes[sl] <= q_hi)
+        assert np.all(ok), (g, np.nonzero(~ok)[0][:5])
+        alt += int(np.count_nonzero(codes[sl] != want))
+    # RoPE, from the fp32 cos/sin the kernel reads
+    cs = cs_row.astype(np.float64)
+    rot = oc.rope_gptj(y, cs[:32], cs[32:])
+    u, w = y[448::2], y[449::2]
+    mag = np.empty(64)
+    mag[0::2] = np.abs(u * cs[:32]) + np.abs(w * cs[32:])
+    mag[1::2] = np.abs(w * cs[:32]) + np.abs(u * cs[32:])
+    near, lo, hi = bf16_neighbours(rot, BAND * mag)
+    got = od.bf16_bits_to_f64(got_payload[448:].view("<u2"))
+    assert np.all((got >= lo) & (got <= hi)), np.nonzero(got != near)[0][:5]
+    alt += int(np.count_nonzero(got != near))
+    return alt
+
+
+def run_case(n_out, c_scale, eps, n_pages, seed, slots=None, pc_rows=600, c=128):
+    g = torch.Generator().manual_seed(seed)
+    comp = torch.randn((n_out, 512), generator=g) * c_scale
+    weight = torch.rand(512, generator=g) * 1.5 + 0.25
+    n_tok = n_out * 3 + 5 if slots is None else slots.shape[0]
+    positions = torch.randint(0, pc_rows, (n_tok,), generator=g)
+    bnd = torch.randperm(n_tok, generator=g)[:n_out]
+    if slots is None:
+        slots = torch.randperm(n_pages * 64, generator=g)[:n_tok]
+    cs = rope_table(pc_rows, seed)
+    kv = torch.randint(0, 256, (n_pages, pkv.KV_PAGE_BYTES), generator=g, dtype=torch.uint8)
+    kv_dev = kv.cuda()
+    pkv.compress_finalize(comp.cuda(), positions.cuda(), bnd.cuda(), weight.cuda(), cs.cuda(),
+                          slots.cuda(), kv_dev, c, eps)
+    torch.cuda.synchronize()
+    out = kv_dev.cpu().numpy()
+    before = kv.numpy()
+    touched = np.zeros_like(before, dtype=bool)
+    alt = 0
+    checked = 0
+    for j in range(n_out):
+        b = int(bnd[j])
+        s = int(slots[b])
+        p = int(positions[b])
+        pc = (p // c) * c
+        if s < 0 or s >= n_pages * 64 or pc >= pc_rows:
+            continue
+        page, po, so = oc.slot_byte_offsets(s)
+        alt += check_output(out[page, po:po + 576], out[page, so:so + 8], f64(comp[j]),
+                            f64(weight), eps, cs[pc].numpy())
+        touched[page, po:po + 576] = True
+        touched[page, so:so + 8] = True
+        checked += 1
+    assert np.array_equal(out[~touched], before[~touched]), "bytes outside the written slots changed"
+    return checked, alt
+
+
+@pytest.mark.parametrize("n_out,c_scale,eps,seed", [
+    (1, 1.0, 1e-6, 1), (64, 1.0, 1e-6, 2), (333, 0.01, 1e-6, 3), (1024, 50.0, 1e-6, 4),
+    (200, 1e-3, 1e-2, 5),
+])
+def test_finalize_bytes(n_out, c_scale, eps, seed):
+    print(f"[gpu] finalize N={n_out} scale={c_scale} eps={eps}", flush=True)
+    checked, alt = run_case(n_out, c_scale, eps, n_pages=max(8, n_out // 16 + 4), seed=seed)
+    assert checked == n_out
+    assert alt <= max(3, checked * 512 // 500), f"{alt} alternative roundings in {checked} outputs"
+
+
+def test_finalize_skips_bad_slots_indices_and_rows():
+    print("[gpu] finalize skips", flush=True)
+    n_pages = 4
+    n_tok = 40
+    slots = torch.randperm(n_pages * 64, generator=torch.Generator().manual_seed(7))[:n_tok]
+    slots[::5] = -1                       # padding tokens
+    slots[1::7] = n_pages * 64 + 3        # past the cache
+    checked, _ = run_case(12, 1.0, 1e-6, n_pages, seed=11, slots=slots, pc_rows=300, c=128)
+    assert 0 < checked < 12
+
+
+def test_finalize_closed_form_is_exact():
+    # c = +-8: rho = 1/8 and y = +-1 (eps = 0, w = 1), every code +-64 with
+    # exponent -6 (byte 121); RoPE with cos 0.6, sin 0.8 gives +-1.4 / +-0.2
+    print("[gpu] finalize closed form", flush=True)
+    g = torch.Generator().manual_seed(3)
+    sign = torch.randint(0, 2, (4, 512), generator=g).to(torch.float32) * 2 - 1
+    comp = 8.0 * sign
+    cs = torch.cat([torch.full((256, 32), 0.6), torch.full((256, 32), 0.8)], 1)
+    positions = torch.tensor([0, 128, 255, 17], dtype=torch.int64)
+    bnd = torch.arange(4, dtype=torch.int64)
+    slots = torch.tensor([0, 63, 64, 130], dtype=torch.int64)
+    kv = torch.zeros((3, pkv.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    pkv.compress_finalize(comp.cuda(), positions.cuda(), bnd.cuda(), torch.ones(512).cuda(),
+                          cs.cuda(), slots.cuda(), kv, 128, 0.0)
+    want = oc.finalize_outputs(comp.double().numpy(), np.ones(512), 0.0, cs.double().numpy(),
+                               positions.numpy(), 128, slots.numpy(),
+                               np.zeros((3, pkv.KV_PAGE_BYTES), dtype=np.uint8))
+    assert np.array_equal(kv.cpu().numpy(), want)
+
+
+def test_compress_then_finalize_end_to_end():
+    # the whole operator on one of the page's shapes: windows compressed by
+    # pkv_compress, packed by pkv_compress_finalize into shuffled KV slots;
+    # the finalizer is checked on the kernel's own compressed values, and
+    # those against the oracle
+    print("[gpu] compress + finalize", flush=True)
+    case = synth.make_compress_case("compress_r4_t32768_c512", device="cuda")
+    comp = pkv.compress(case.state_cache, case.token_to_req, case.positions, case.boundaries,
+                        case.block_table, case.compress_ratio)
+    n = case.num_outputs
+    t = case.positions.shape[0]
+    g = torch.Generator().manual_seed(5)
+    n_pages = (n + 63) // 64 + 2
+    slots = torch.full((t,), -1, dtype=torch.int64)
+    slots[case.boundaries.cpu()] = torch.randperm(n_pages * 64, generator=g)[:n]
+    cs = rope_table(int(case.positions.max()) + 1, 5)
+    weight = torch.rand(512, generator=g) + 0.5
+    kv = torch.zeros((n_pages, pkv.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    pkv.compress_finalize(comp, case.positions, case.boundaries, weight.cuda(), cs.cuda(),
+                          slots.cuda(), kv, case.compress_ratio, 1e-6)
+    torch.cuda.synchronize()
+    out = kv.cpu().numpy()
+    comp64 = f64(comp)
+    alt = 0
+    for j in range(n):
+        b = int(case.boundaries[j])
+        page, po, so = oc.slot_byte_offsets(int(slots[b]))
+        pc = (int(case.positions[b]) // 512) * 512
+        alt += check_output(out[page, po:po + 576], out[page, so:so + 8], comp64[j],
+                            f64(weight), 1e-6, cs[pc].numpy())
+    assert alt <= max(3, n * 512 // 500)
