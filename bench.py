@@ -255,7 +255,9 @@ def measure_prefill(name, steps, warmup, torch, pkv, synth):
 def measure_compress(name, steps, warmup, torch, pkv, synth):
     """Paged window compression of one of the 12 shapes, graph-replayed over
     cold replicas of the state cache. Algorithmic bytes: every window row read
-    once (4 KiB: 512 fp32 values + 512 fp32 scores) plus the fp32 output."""
+    once (4 KiB: 512 fp32 values + 512 fp32 scores) plus the fp32 output.
+    Also times the finalizer alone (RMSNorm, INT8/RoPE packing, KV-page
+    scatter of every output) and the whole operator (both launches)."""
     case = synth.make_compress_case(name, device="cuda")
     n, c = case.num_outputs, case.compress_ratio
     rows = sum(min(int(p) + 1, c) for p in case.positions[case.boundaries].tolist())
@@ -268,37 +270,63 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
     out = torch.empty((n, case.head_dim), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(pkv.compress_workspace_bytes(prm), 256), dtype=torch.uint8,
                      device="cuda")
+    # the finalizer's inputs: fp32 weight and cos/sin table, every output
+    # packed into its own slot of a shuffled KV page pool
+    gen = torch.Generator().manual_seed(7)
+    t = case.positions.shape[0]
+    weight = (torch.rand(case.head_dim, generator=gen) + 0.5).cuda()
+    rows = int(case.positions.max()) + 1
+    th = torch.rand((rows, 32), generator=gen) * 6.283
+    cos_sin = torch.cat([torch.cos(th), torch.sin(th)], 1).cuda()
+    kv_pages = (n + 63) // 64 + 1
+    slots = torch.full((t,), -1, dtype=torch.int64)
+    slots[case.boundaries.cpu()] = torch.randperm(kv_pages * 64, generator=gen)[:n]
+    slots = slots.cuda()
+    kv = torch.zeros((kv_pages, pkv.KV_PAGE_BYTES), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.Stream()
 
     def step(i):
         pkv.compress(caches[i % copies], case.token_to_req, case.positions, case.boundaries,
                      case.block_table, c, out=out, workspace=ws)
 
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            step(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            step(i)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        g.replay()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    def finalize(i):
+        pkv.compress_finalize(out, case.positions, case.boundaries, weight, cos_sin, slots, kv, c)
+
+    def operator(i):
+        step(i)
+        finalize(i)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    us = timed(step)
+    us_fin = timed(finalize)
+    us_op = timed(operator)
     gbps = nbytes / (us * 1e-6) / 1e9
     res = {"workload": name, "kernel": "compress_split_kernel" + ("+compress_combine_kernel"
                                                                  if splits > 1 else ""),
-           "num_outputs": n, "compress_ratio": c, "tokens": int(case.positions.shape[0]),
+           "num_outputs": n, "compress_ratio": c, "tokens": int(t),
            "num_splits": splits, "workgroups": n * splits, "cold_copies": copies,
            "steps": steps, "algorithmic_bytes": nbytes, "us_per_call": round(us, 3),
-           "gbps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
+           "gbps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
+           "finalize_us": round(us_fin, 3), "operator_us": round(us_op, 3)}
     log(json.dumps(res))
-    del g, caches, case, out, ws
+    del caches, case, out, ws, kv
     torch.cuda.empty_cache()
     return res
 
