@@ -93,3 +93,23 @@ def test_prefill_page_size_invariant_and_repeatable():
         assert np.array_equal(bits(again), outs[-1])
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+def test_prefill_score_jump_takes_the_exact_pass():
+    # one key of a later tile scores about 60 log2 units above everything in
+    # the first tile for one query: weights relative to the first tile's max
+    # would pass 2^40, so that workgroup redoes its block with exact maxima
+    print("[gpu] prefill score jump", flush=True)
+    nq, length, bsz = 64, 300, 64
+    case, q_new = synth.build_prefill_case("pfj", nq, length, bsz, seed=12, device="cuda")
+    i, t = 10, 100                                  # query 10 sits at position 246
+    q = q_new[i, 0].float()
+    k = q * (60.0 * 16.0 / (1.4426950408889634 * float((q * q).sum())))
+    k = k.to(torch.bfloat16)
+    case.k_logical[t, 0] = k                        # KV head 0 of the one sequence
+    page = int(case.block_table[0, t // bsz])
+    case.k_cache[page, t % bsz, 0] = k
+    out, out32 = run_prefill(case, q_new)
+    s = float((q * k.float()).sum()) / 16.0 * 1.4426950408889634
+    assert s > 50.0, s
+    check(case, q_new, out, out32)
