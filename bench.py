@@ -456,6 +456,96 @@ def cpu_baseline_parallel(budget_s=10.0):
                       f"(the most this one-sequence step splits into), {el:.1f} s"}
 
 
+def cpu_baseline_rows(budget_s=3.0):
+    """The oracles of the rows built beside decode, as they stand, timed on the
+    host with one BLAS thread on bounded samples of their bench workloads and
+    scaled to one call: prefill on sampled query rows of q = 4096, L = 32768;
+    the append scatter on a slice of the 32768-token chunk; the compression
+    and its finalizer on sampled outputs of 8 x 16384 tokens at C = 128.
+    Input conversion to fp64 is inside each timed region."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import append as oa
+    from oracle import compress as oc
+    from oracle import decode as od
+    from oracle import prefill as opf
+    from paged_kv_cache_36_amd import synth
+
+    def timed(fn):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                return el / n, n, el
+
+    out = {}
+    ncpu, model = host_cpu()
+    with threadpool_limits(limits=1):
+        # prefill: 4 query rows (all 24 heads) per call of the oracle
+        case, q_new = synth.make_prefill_case("prefill_q4096_l32768_b832", device="cpu")
+        qb = q_new.view(torch.int16).numpy().view(np.uint16)
+        kb = case.k_logical.view(torch.int16).numpy().view(np.uint16)
+        vb = case.v_logical.view(torch.int16).numpy().view(np.uint16)
+        rows = [0, 1365, 2730, 4095]
+        conv = {}
+
+        def convert():
+            conv["q"] = od.bf16_bits_to_f64(qb)
+            conv["k"] = od.bf16_bits_to_f64(kb)
+            conv["v"] = od.bf16_bits_to_f64(vb)
+
+        tc, _, _ = timed(convert)
+        t, n, el = timed(lambda: opf.attention_prefill(conv["q"], conv["k"], conv["v"],
+                                                       case.scale, rows=rows))
+        out["prefill_q4096_l32768_b832"] = {
+            "value": round((tc + t / len(rows) * 4096) * 1e6, 1), "unit": "us/call", "cores": 1,
+            "kind": "oracle",
+            "sample": f"bf16->fp64 conversion of q, K, V timed once ({tc * 1e3:.0f} ms) plus {n} "
+                      f"oracle calls on {len(rows)} of 4096 query rows scaled to 4096, {el:.1f} s"}
+        del conv
+        del case, q_new, qb, kb, vb
+        # append: 2048 of the 32768 new tokens into page-832 pages
+        rng = np.random.default_rng(0)
+        ntok, bsz = 2048, 832
+        pool = np.zeros((40, bsz, 4, 256), dtype=np.uint16)
+        new = rng.integers(0, 1 << 16, size=(ntok, 4, 256), dtype=np.uint16)
+        slots = oa.slots_for_positions(rng.permutation(40), np.arange(ntok), bsz)
+        t, n, el = timed(lambda: oa.append_rows(pool, new, slots, bsz))
+        out["append_chunk_32768tok_b832"] = {
+            "value": round(t / ntok * 32768 * 1e6, 1), "unit": "us/call", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} oracle calls on {ntok} of 32768 tokens (pool copy included), scaled, {el:.1f} s"}
+        # compression + finalizer: 16 of the 1024 outputs
+        case = synth.make_compress_case("compress_r8_t131072_c128", device="cpu")
+        states = case.states.numpy()
+        per_req = [states[lo:hi] for lo, hi in (case.req_range(r) for r in range(len(case.lens)))]
+        bnd = case.boundaries.numpy()[::64]
+        tok = case.token_to_req.numpy()
+        pos = case.positions.numpy()
+        t, n, el = timed(lambda: oc.compress_outputs(per_req, tok, pos, bnd, 128))
+        out["compress_r8_t131072_c128"] = {
+            "value": round(t / len(bnd) * case.num_outputs * 1e6, 1), "unit": "us/call",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n} oracle calls on {len(bnd)} of {case.num_outputs} outputs, scaled, {el:.1f} s"}
+        comp = np.random.default_rng(1).standard_normal((len(bnd), 512))
+        cs = np.random.default_rng(2).standard_normal((int(pos.max()) + 1, 64))
+        kv = np.zeros((len(bnd) // 64 + 2, oc.KV_PAGE_BYTES), dtype=np.uint8)
+        t, n, el = timed(lambda: oc.finalize_outputs(comp, np.ones(512), 1e-6, cs, pos[bnd], 128,
+                                                     np.arange(len(bnd)), kv))
+        out["compress_finalize_1024"] = {
+            "value": round(t / len(bnd) * 1024 * 1e6, 1), "unit": "us/call", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} oracle calls on {len(bnd)} of 1024 outputs, scaled, {el:.1f} s"}
+    for v in out.values():
+        v["host_cpus"], v["cpu_model"] = ncpu, model
+    return out
+
+
 def traffic_for(res):
     """HBM bytes per split launch from the committed counter runs, or None when
     the kernel source changed since they were taken."""
@@ -549,6 +639,7 @@ def main():
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel()
+    cpu_rows = None if args.no_cpu_baseline or args.workloads != "all" else cpu_baseline_rows()
 
     us = main_res["us_per_step"]
     traffic = traffic_for(main_res)
@@ -587,6 +678,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "cpu_baseline_parallel": cpu_par,
+        "cpu_baseline_rows": cpu_rows,
         "read_probe_gbps": probe,
         "workloads": [main_res] + extra,
         "append": appends,
