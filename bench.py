@@ -568,7 +568,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", default="all",
-                    help="main, all, prefill, compress, or one workload name (timed alone)")
+                    help="main, decode (all decode workloads), all, prefill, compress, or one "
+                         "workload name (timed alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also launch the plain copy kernel (counter calibration runs)")
@@ -593,7 +594,7 @@ def main():
     if args.copy_probe:
         copy_probe(torch, pkv)
 
-    if args.workloads not in ("main", "all", "prefill", "compress"):
+    if args.workloads not in ("main", "all", "decode", "prefill", "compress"):
         name = args.workloads
         if name in synth.WORKLOADS:
             res = measure(name, args.steps, args.warmup, torch, pkv, synth)
@@ -612,7 +613,7 @@ def main():
         return
     main_res = measure(MAIN, args.steps, args.warmup, torch, pkv, synth)
     extra = []
-    if args.workloads == "all":
+    if args.workloads in ("all", "decode"):
         caps = {"batched_8seq_t131072_b832": 200, "wide_64seq_b832_p4096": 20}
         for name in EXTRA:
             extra.append(measure(name, min(args.steps, caps.get(name, 400)), args.warmup,
