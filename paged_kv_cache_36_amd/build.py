@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # no packed-fp32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with AGPR accumulators the prefill
+    # loop copied its whole accumulator out and back on every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

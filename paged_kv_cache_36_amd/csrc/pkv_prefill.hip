@@ -8,28 +8,44 @@
 // Optimization", "Starting from Attention"; the online max / denominator /
 // numerator update: same page, "Online Softmax: Streaming Away the Window").
 //
-// Work split. One workgroup (4 waves) per (query head, block of 128 queries);
-// the blocks with the longest causal ranges are launched first. Wave w owns
-// 32 queries, the 32 columns of its MFMA tiles. Per tile of 32 keys (small
-// enough that the whole working set, accumulator included, stays in VGPRs):
-//  - the workgroup stages the K and V rows of the tile in LDS (rows looked up
-//    through the block table one by one, so any page size works); the next
-//    tile's rows are loaded into registers while the current one is used,
-//  - S^T (32 keys x 32 queries) = K Q^T by 16 v_mfma_f32_32x32x16_bf16, K (A
-//    operand) and the wave's Q^T fragments (B operand) read from LDS, where
-//    the block's queries are staged once; lane l then holds query l % 32 and
-//    16 of the tile's keys,
+// Work split. One workgroup of 8 waves per (query head, block of 128
+// queries): wave (g, k) owns queries 32 g .. 32 g + 31 (the 32 columns of its
+// MFMA tiles, their Q^T fragments held in registers) and keys 32 k .. 32 k +
+// 31 of every 64-key tile, so the two waves sharing a SIMD interleave their
+// matrix and vector phases. Tiles stream through two LDS stages that
+// direct-to-LDS loads (global_load_lds_dwordx4) fill one tile ahead: one
+// barrier per tile and no register staging. Per wave and tile:
+//  - S^T (32 keys x 32 queries) = K Q^T by 16 v_mfma_f32_32x32x16_bf16 (K, the
+//    A operand, from LDS); lane l then holds query l % 32 and 16 of the keys,
 //  - online softmax in log2 units per query (one lane pair), the causal mask
-//    only on tiles that reach past the block's first query,
+//    only where the keys reach past the block's first query,
 //  - O^T (256 dims x 32 queries) += V^T P^T by 16 MFMAs: p is rounded to bf16
 //    straight from the S^T registers (the B operand needs exactly the keys the
 //    lane holds, in the order k = keys 4h..4h+3, 8+4h..8+4h+3 of each 16-key
 //    chunk, h = l / 32), and V^T comes from LDS through the transposing read
 //    in that same key order.
-// The accumulator belongs to the lane's query, so the rescale is per lane.
+// At the end the two key halves of each query group merge through LDS.
+//
+// LDS layout. A direct load writes 64 consecutive 16-byte slots; a tile is
+// stored as 1 KiB blocks of 8 rows x 8 pieces (128 contiguous bytes of each
+// row, so every load reads whole cache lines):
+//  - K: block (piece group pg, row group rg) at pg * 8 + rg; piece p of row r
+//    in slot ((p % 8) ^ (rg & 1)) * 8 + r % 8. The A-operand read of step ks
+//    (rows 0..31, pieces 2 ks, 2 ks + 1) is then a fixed per-lane offset plus
+//    a constant, and each 16 lanes hit 16 distinct slots of 256 bytes.
+//  - V: block (key group kb, piece group pb) at kb * 4 + pb; piece p of key
+//    r in slot (r % 8) * 8 + ((p % 8) ^ 4 ((r >> 1) & 1)). Each half of a
+//    transposing read (4 keys x 64 bytes) hits 16 distinct slots.
+//
+// Grid order. The workgroups of one KV head read the same keys from position
+// 0 upwards; blocks are dealt to XCDs (workgroup b runs on XCD b % 8) so that
+// each XCD serves one KV head. Within a head the longest causal ranges go
+// first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -37,24 +53,29 @@
 namespace pkv {
 namespace {
 
-constexpr int kPfThreads = 256;                 // 4 waves
+constexpr int kPfThreads = 512;                 // 8 waves: 4 query groups x 2 key halves
 constexpr int kPfCols = 32;                     // queries per wave
 constexpr int kPfQueries = 4 * kPfCols;         // queries per workgroup
-constexpr int kPfKeys = 32;                     // keys per tile (one MFMA block)
-// LDS row strides (elements). K: 528 bytes, so the 16 rows one A-operand
-// read touches per 16 lanes start 4 banks apart. V: 576 bytes, so the 4 rows x
-// 2 dim groups of a transposing read cover distinct banks.
-constexpr int kPfKStride = kHeadSize + 8;
-constexpr int kPfVStride = kHeadSize + 32;
+constexpr int kPfWaveKeys = 32;                 // keys per wave and tile
+constexpr int kPfKeys = 2 * kPfWaveKeys;        // keys per tile
+constexpr int kXcds = 8;                        // XCDs workgroups are dealt to, round robin
+constexpr int kBlockBytes = 1024;               // 8 rows x 8 pieces of 16 bytes
+constexpr int kTileBytes = kPfKeys * kHeadSize * 2;   // 32 KiB of K (or of V)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-struct PrefillLds {
-  uint16_t q[kPfQueries * kPfKStride];   // the block's queries (same padded rows as K)
-  uint16_t k[kPfKeys * kPfKStride];
-  uint16_t v[kPfKeys * kPfVStride];
+struct PrefillStage {
+  char k[kTileBytes];
+  char v[kTileBytes];
 };
+// the tiles, or after them the merge of the two key halves
+union PrefillLds {
+  PrefillStage stage[2];
+  float merge[4][kPfCols * kHeadSize + 128];
+};
+static_assert(sizeof(PrefillLds) <= 160 * 1024, "LDS budget of one workgroup");
 
 // The running max is only moved when a tile's max exceeds it by more than
 // this (log2 units): the weights exp2(x - m) then stay below 2^8, which bf16
@@ -67,20 +88,53 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// One direct-to-LDS load (64 lanes x 16 bytes into 1 KiB of LDS at lds_dst).
+// Written as asm so the compiler does not order later LDS reads behind it:
+// the loop waits for these loads itself (vmcnt(0) before each barrier), and
+// they only ever fill the stage no wave is reading.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(dst));
+}
+
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// (query head, query block) of workgroup b; false for grid padding. XCD x
+// serves KV head x % hkv, so one L2 sees every request for that head's tiles.
+__device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int& h, int& qb) {
+  const int per_kv = kGroup * nqb;
+  if (kXcds % hkv == 0) {
+    const int x = b % kXcds;
+    const int j = (b / kXcds) * (kXcds / hkv) + x / hkv;
+    if (j >= per_kv) return false;
+    h = (x % hkv) * kGroup + j % kGroup;
+    qb = nqb - 1 - j / kGroup;
+    return true;
+  }
+  const int hq = hkv * kGroup;
+  h = b % hq;
+  qb = nqb - 1 - b / hq;
+  return true;
+}
+
+template <bool kFold>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) PrefillLds lds;
+  __shared__ __attribute__((aligned(1024))) PrefillLds lds;
   const int hq = a.num_kv_heads * kGroup;
   const int nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
-  const int h = blockIdx.x % hq;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x / hq);   // longest ranges first
+  int h, qb;
+  if (!block_of(blockIdx.x, a.num_kv_heads, nqb, h, qb)) return;
   const int g = h / kGroup;
   const int lane = lane_id();
-  const int w = wave_id();
+  const int wid = wave_id();
+  const int w = wid & 3;           // query group
+  const int kh = wid >> 2;         // key half of each tile
   const int col = lane & 31;
   const int half = lane >> 5;
   const int q0 = qb * kPfQueries;
@@ -90,77 +144,113 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int pos = q_valid ? first_pos + qi : -1;
   const int block_first = first_pos + q0;             // position of the block's first query
   const int kend = first_pos + min(q0 + kPfQueries, a.num_q);   // keys the block needs
+  const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
   const int row_elems = a.num_kv_heads * kHeadSize;
+  const int bsz = a.block_size;
 
-  // The block's queries go to LDS once (rows past the last query are zero);
-  // each wave reads its Q^T fragments (B operand: lane = query column, dims
-  // 16 ks + 8 half .. + 7) from there per tile, which keeps them out of the
-  // registers the accumulator needs.
+  // Q^T fragments (B operand: lane = query column, dims 16 ks + 8 half .. + 7)
+  // stay in registers; rows past the last query repeat it (never stored).
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow =
+        a.q + (static_cast<int64_t>(min(qi, a.num_q - 1)) * hq + h) * kHeadSize + 8 * half;
 #pragma unroll
-  for (int i = 0; i < kPfQueries * kHeadSize / 8 / kPfThreads; ++i) {
-    const int piece = threadIdx.x + kPfThreads * i;   // 16-byte piece of the block's rows
-    const int row = piece >> 5;
-    const int c8 = (piece & 31) * 8;
-    const int qrow = q0 + row;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qrow < a.num_q)
-      x = *reinterpret_cast<const u32x4*>(a.q + (static_cast<int64_t>(qrow) * hq + h) * kHeadSize + c8);
-    *reinterpret_cast<u32x4*>(lds.q + row * kPfKStride + c8) = x;
+    for (int ks = 0; ks < 16; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * ks));
   }
-  const uint16_t* q_frag = lds.q + (kPfCols * w + col) * kPfKStride + 8 * half;
 
-  // Tile staging: thread (row tr, part) moves the 16-byte pieces 64 i + 8 part
-  // (i = 0..3) of the head's 256 dims of row tr, for K and for V: every load
-  // instruction covers 8 rows x 128 contiguous bytes.
-  const int tr = threadIdx.x >> 3;
-  const int part = threadIdx.x & 7;
-  u32x4 kr[4], vr[4];
-  // (logical page, offset) of the thread's row, moved by one tile per fetch
-  int lp_r = tr / a.block_size;
-  int off_r = tr - lp_r * a.block_size;
-  auto fetch = [&](int t0) {
-    const int t = t0 + tr;
-    const int lp = lp_r, off = off_r;
-    off_r += kPfKeys;
-    while (off_r >= a.block_size) {
-      off_r -= a.block_size;
-      ++lp_r;
-    }
-    if (t < kend) {
-      const int64_t page = a.block_table[lp];
-      const uint16_t* ks = a.k + page * a.k_page_stride + static_cast<int64_t>(off) * row_elems +
-                           g * kHeadSize + 8 * part;
-      const uint16_t* vs = a.v + page * a.v_page_stride + static_cast<int64_t>(off) * row_elems +
-                           g * kHeadSize + 8 * part;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kr[i] = *reinterpret_cast<const u32x4*>(ks + 64 * i);
-        vr[i] = *reinterpret_cast<const u32x4*>(vs + 64 * i);
-      }
-    } else {   // past the last key: zeros (finite; their weights are 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  // Direct loads: wave wid fills K row group wid (rows 8 wid + s % 8, all
+  // four piece groups) and V key group wid (keys 8 wid + s / 8) of each tile.
+  // Rows at or past kend read row kend - 1 instead (finite; weight 0).
+  const int k_row = 8 * wid + (lane & 7);
+  const int v_row = 8 * wid + (lane >> 3);
+  const int k_piece = ((lane >> 3) ^ (wid & 1));             // + 8 pg
+  const int v_piece = ((lane & 7) ^ (4 * ((lane >> 4) & 1)));   // + 8 pb
+  const int last_lp = (kend - 1) / bsz;
+  const int last_off = kend - 1 - last_lp * bsz;
+  const int nblocks = (a.seq_len + bsz - 1) / bsz;
+  const int64_t last_page = a.block_table[last_lp];
+  // logical page and offset of row 8 wid of the next tile to load
+  int lpw = (8 * wid) / bsz;
+  int offw = 8 * wid - lpw * bsz;
+  const int step_pages = kPfKeys / bsz, step_off = kPfKeys % bsz;
+  // page ids of logical pages win_base .. win_base + 63, one per lane
+  int win_base = 0;
+  int win = a.block_table[min(lane, nblocks - 1)];
+
+  // Source rows of the next tile's loads and the stage they fill; the eight
+  // loads themselves are spread over the S^T products (load()), so no wave
+  // stalls on a full memory queue right after the barrier.
+  struct NextTile {
+    const uint16_t* ksrc;
+    const uint16_t* vsrc;
+    char* kdst;
+    char* vdst;
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(lds.k + tr * kPfKStride + 64 * i + 8 * part) = kr[i];
-      *reinterpret_cast<u32x4*>(lds.v + tr * kPfVStride + 64 * i + 8 * part) = vr[i];
+  auto prepare = [&](int tt) {
+    const int t0 = tt * kPfKeys;
+    if (lpw + 8 - win_base >= 64) {
+      win_base = lpw;
+      win = a.block_table[min(win_base + lane, nblocks - 1)];
     }
+    // every lane takes part in the window lookup (a lane reading from an
+    // inactive lane would get nothing), then rows past kend switch to kend - 1
+    auto locate = [&](int r, int64_t& page, int& off) {
+      int lp = lpw;
+      off = offw + (r & 7);
+      while (off >= bsz) {
+        off -= bsz;
+        ++lp;
+      }
+      const int id = __builtin_amdgcn_ds_bpermute(4 * (lp - win_base), win);
+      const bool live = t0 + r < kend;
+      page = live ? static_cast<int64_t>(id) : last_page;
+      off = live ? off : last_off;
+    };
+    int64_t kpage, vpage;
+    int koff, voff;
+    locate(k_row, kpage, koff);
+    locate(v_row, vpage, voff);
+    const uint16_t* ksrc = a.k + kpage * a.k_page_stride +
+                           (static_cast<int64_t>(koff) * row_elems + g * kHeadSize + 8 * k_piece);
+    const uint16_t* vsrc = a.v + vpage * a.v_page_stride +
+                           (static_cast<int64_t>(voff) * row_elems + g * kHeadSize + 8 * v_piece);
+    PrefillStage& st = lds.stage[tt & 1];
+    offw += step_off;
+    lpw += step_pages;
+    if (offw >= bsz) {
+      offw -= bsz;
+      ++lpw;
+    }
+    return NextTile{ksrc, vsrc, st.k + wid * kBlockBytes, st.v + wid * 4 * kBlockBytes};
+  };
+  // load i of a tile: K piece group i / 2 (even i) or V piece group i / 2 (odd i)
+  auto load = [&](const NextTile& nt, int i) {
+    const int pg = i >> 1;
+    if (i & 1)
+      dma16(nt.vsrc + 64 * pg, nt.vdst + pg * kBlockBytes);
+    else
+      dma16(nt.ksrc + 64 * pg, nt.kdst + pg * 8 * kBlockBytes);
   };
 
-  // transposing-read offsets (elements): 16-lane group G = lane / 16 reads
-  // dims 16 (G & 1) + 0..15 of a 32-dim block for keys 4 (G >> 1) + 0..3
-  // (+ 8 for the second read) of a 16-key chunk; lane j of the group supplies
-  // the address of key j / 4, dims 4 (j % 4) .. + 3
+  // K A-operand read of step ks: row 32 kh + col, pieces 2 ks + half, at
+  // block (ks / 4) * 8 + rg, slot (2 (ks % 4) + (half ^ (rg & 1))) * 8 + row % 8
+  const int krow = kPfWaveKeys * kh + col;
+  const int krg = krow >> 3;
+  const int k_lane = krg * kBlockBytes + (((half ^ (krg & 1)) * 8 + (krow & 7)) * 16);
+  // V^T transposing reads: 16-lane group G = lane / 16 reads dims 16 (G & 1)
+  // + 0..15 of a 32-dim block for keys 4 (G >> 1) + 0..3 (+ 8 for the second
+  // read) of a 16-key chunk; lane j of the group supplies the address of key
+  // j / 4, dims 4 (j % 4) .. + 3: piece 4 db + 2 (G & 1) + (j % 4) / 2, half
+  // j % 2 of it. Within its 8-key group the key is r8 = 4 (G >> 1) + j / 4,
+  // whose swizzle flips piece bit 2 when (r8 >> 1) & 1 = (j >> 3) & 1.
   const int vgrp = lane >> 4;
   const int vj = lane & 15;
-  const int v_off = (4 * (vgrp >> 1) + (vj >> 2)) * kPfVStride + 16 * (vgrp & 1) + 4 * (vj & 3);
-  const int k_off = col * kPfKStride + 8 * half;   // A-operand read: key row col, 8 dims
+  const int r8 = 4 * (vgrp >> 1) + (vj >> 2);
+  const int vfb = (vj >> 3) & 1;
+  const int vp_lo = 2 * (vgrp & 1) + ((vj & 3) >> 1);
+  const int v_lane0 = (r8 * 8 + 4 * vfb + vp_lo) * 16 + 8 * (vj & 1);          // even db
+  const int v_lane1 = (r8 * 8 + 4 * (vfb ^ 1) + vp_lo) * 16 + 8 * (vj & 1);    // odd db
 
   f32x16 acc[8];
 #pragma unroll
@@ -168,69 +258,48 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY;   // running max (log2 units) of this lane's query, moved lazily
   float lsum = 0.f;      // this lane's share of the weight sum
 
-  // One tile's scores S^T (scaled to log2 units, causal mask applied);
-  // register r holds key t0 + 8 (r / 4) + 4 half + r % 4. Returns the tile max
-  // of the lane's query.
-  auto scores = [&](int t0, f32x16& s) {
-    s = f32x16{};
+  // One tile. kMasked: the causal mask may cut the wave's keys (only the
+  // tiles that reach past the block's first query). kFold (scale > 0): the
+  // scores stay unscaled, their max is scaled once, and each weight is
+  // exp2(fma(s, scale, -m)).
+  auto step = [&](int tt, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    // this wave's loads of tile tt are done; the barrier makes every wave's
+    // rows visible and frees the stage of tile tt - 1
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    // after the last tile these loads fill the free stage with row kend - 1
+    // (every row of tile ntiles is past kend): no branch around them
+    const NextTile nt = prepare(tt + 1);
+    const PrefillStage& st = lds.stage[tt & 1];
+    const int t0 = tt * kPfKeys + kPfWaveKeys * kh;   // this wave's first key
+
+    // S^T = K Q^T; register r holds key t0 + 8 (r / 4) + 4 half + r % 4
+    f32x16 s = f32x16{};
+    const char* kbase = st.k + k_lane;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 qf = as_bf16x8(*reinterpret_cast<const u32x4*>(q_frag + 16 * ks));
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(lds.k + k_off + 16 * ks);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf, s, 0, 0, 0);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kbase + (ks >> 2) * 8 * kBlockBytes +
+                                                        (ks & 3) * 256);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], s, 0, 0, 0);
+      if (ks & 1) load(nt, ks >> 1);
     }
+    if constexpr (!kFold) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] *= a.scale_log2;
-    if (t0 + kPfKeys - 1 > block_first) {   // tile reaches past the block's first query
+      for (int r = 0; r < 16; ++r) s[r] *= a.scale_log2;
+    }
+    if constexpr (kMasked) {
+      if (t0 + kPfWaveKeys - 1 > block_first) {   // keys reach past the block's first query
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (t0 + 8 * (r >> 2) + 4 * half + (r & 3) > pos) s[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if (t0 + 8 * (r >> 2) + 4 * half + (r & 3) > pos) s[r] = -INFINITY;
+      }
     }
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    return fmaxf(tmax, __shfl_xor(tmax, 32));
-  };
-
-  // p = exp2(x - m) rounded to bf16 as the P^T operand (chunk c: keys
-  // 16 c .. 16 c + 15 = registers 8 c .. 8 c + 7), then O^T += V^T P^T.
-  auto accumulate = [&](const f32x16& s, float m_ref) {
-    bf16x8 pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = exp2_fast(s[8 * c + e] - m_ref);
-        lsum += p[e];
-      }
-      const u32x4 packed = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                            pack_bf16(p[6], p[7])};
-      pb[c] = as_bf16x8(packed);
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint16_t* vp = lds.v + 16 * c * kPfVStride + v_off;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db));
-        const s16x4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * kPfVStride + 32 * db));
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[db], 0, 0, 0);
-      }
-    }
-  };
-
-  fetch(0);
-  for (int t0 = 0; t0 < kend; t0 += kPfKeys) {
-    __syncthreads();   // the previous tile is consumed
-    stash();
-    __syncthreads();
-    if (t0 + kPfKeys < kend) fetch(t0 + kPfKeys);   // in flight during this tile's math
-    f32x16 s;
-    const float tmax = scores(t0, s);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    if constexpr (kFold) tmax *= a.scale_log2;
     if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleLog2)) {   // rare after the first tile
       const float m_new = fmaxf(m, tmax);
       const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m - m_new);
@@ -239,12 +308,82 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
       for (int db = 0; db < 8; ++db) acc[db] *= alpha;
       m = m_new;
     }
-    accumulate(s, m == -INFINITY ? 0.f : m);   // nothing seen yet: weights 0
-  }
+    const float m_ref = m == -INFINITY ? 0.f : m;   // nothing seen yet: weights 0
 
-  // o = acc / l: register r of block db holds dim 32 db + 8 (r / 4) + 4 half + r % 4
+    // p = exp2(x - m) rounded to bf16 as the P^T operand (chunk c: keys
+    // 16 c .. 16 c + 15 = registers 8 c .. 8 c + 7), then O^T += V^T P^T.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (kFold)
+          p[e] = exp2_fast(fmaf(s[8 * c + e], a.scale_log2, -m_ref));
+        else
+          p[e] = exp2_fast(s[8 * c + e] - m_ref);
+        lsum += p[e];
+      }
+      const u32x4 packed = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                            pack_bf16(p[6], p[7])};
+      pb[c] = as_bf16x8(packed);
+    }
+    // key group of chunk c, read hi: 4 kh + 2 c + hi; piece group db / 2
+    const char* vbase = st.v + (4 * kh) * 4 * kBlockBytes;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const char* vp = vbase + (db & 1 ? v_lane1 : v_lane0) + (db >> 1) * kBlockBytes;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const char* vc = vp + (2 * c) * 4 * kBlockBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vc);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vc + 4 * kBlockBytes));
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[c], acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // tiles whose 64 keys all precede the block's first query need no mask
+  const int n_open = min(ntiles, (block_first + 1) / kPfKeys);
+  {
+    const NextTile nt = prepare(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load(nt, i);
+  }
+  for (int tt = 0; tt < n_open; ++tt) step(tt, std::false_type{});
+  for (int tt = n_open; tt < ntiles; ++tt) step(tt, std::true_type{});
+
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the spare loads into LDS are done
+  // The two key halves of a query group merge through LDS (the tiles are
+  // done): the second half's wave leaves (m, l, acc) there, the first half's
+  // wave rescales both to the larger max and writes the output.
   lsum += __shfl_xor(lsum, 32);
-  if (!q_valid) return;
+  __syncthreads();
+  float* mbuf = lds.merge[w];
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mbuf[(db * 16 + r) * 64 + lane] = acc[db][r];
+    mbuf[kPfCols * kHeadSize + lane] = m;
+    mbuf[kPfCols * kHeadSize + 64 + lane] = lsum;
+  }
+  __syncthreads();
+  if (kh == 1 || !q_valid) return;
+  {
+    const float m2 = mbuf[kPfCols * kHeadSize + lane];
+    const float l2 = mbuf[kPfCols * kHeadSize + 64 + lane];
+    const float mx = fmaxf(m, m2);   // finite: key 0 is visible to every query
+    const float f1 = exp2_fast(m - mx), f2 = exp2_fast(m2 - mx);
+    lsum = lsum * f1 + l2 * f2;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * f1 + mbuf[(db * 16 + r) * 64 + lane] * f2;
+  }
+  // o = acc / l: register r of block db holds dim 32 db + 8 (r / 4) + 4 half + r % 4
   const float inv = 1.f / lsum;   // lsum >= 1: the maximum key has weight 1
   const int64_t orow = (static_cast<int64_t>(qi) * hq + h) * kHeadSize + 4 * half;
 #pragma unroll
@@ -268,10 +407,20 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_q <= 0) return hipSuccess;
-  const int64_t blocks = static_cast<int64_t>(a.num_kv_heads) * kGroup *
-                         ((a.num_q + kPfQueries - 1) / kPfQueries);
-  hipLaunchKernelGGL(prefill_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads), 0,
-                     stream, a);
+  const int64_t nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
+  int64_t blocks = static_cast<int64_t>(a.num_kv_heads) * kGroup * nqb;
+  if (kXcds % a.num_kv_heads == 0) {
+    // every XCD gets the same number of slots; slots past a head's list exit
+    const int64_t per_xcd =
+        (kGroup * nqb + kXcds / a.num_kv_heads - 1) / (kXcds / a.num_kv_heads);
+    blocks = per_xcd * kXcds;
+  }
+  if (a.scale_log2 > 0.f)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 

@@ -95,10 +95,11 @@ def test_prefill_page_size_invariant_and_repeatable():
         assert np.array_equal(o, outs[0])
 
 
-def test_prefill_score_jump_takes_the_exact_pass():
+def test_prefill_score_jump_rescales_the_accumulator():
     # one key of a later tile scores about 60 log2 units above everything in
     # the first tile for one query: weights relative to the first tile's max
-    # would pass 2^40, so that workgroup redoes its block with exact maxima
+    # would pass 2^40, so the running max must move and the accumulator and
+    # the weight sum be rescaled
     print("[gpu] prefill score jump", flush=True)
     nq, length, bsz = 64, 300, 64
     case, q_new = synth.build_prefill_case("pfj", nq, length, bsz, seed=12, device="cuda")
@@ -112,4 +113,16 @@ def test_prefill_score_jump_takes_the_exact_pass():
     out, out32 = run_prefill(case, q_new)
     s = float((q * k.float()).sum()) / 16.0 * 1.4426950408889634
     assert s > 50.0, s
+    check(case, q_new, out, out32)
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0 / 16.0, 1.0 / 64.0])
+def test_prefill_other_scales(scale):
+    # a positive scale folds into the exponent's fma; zero and negative scales
+    # take the kernel's other instantiation (scores scaled before the max)
+    print(f"[gpu] prefill scale {scale}", flush=True)
+    nq, length, bsz = 300, 2100, 784
+    case, q_new = synth.build_prefill_case("pfs", nq, length, bsz, seed=21, device="cuda")
+    case.scale = scale
+    out, out32 = run_prefill(case, q_new)
     check(case, q_new, out, out32)
