@@ -187,8 +187,27 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     char* kdst;
     char* vdst;
   };
+  // the previous tile's source rows: when this tile's rows sit 64 rows
+  // further in the same pages and none is clamped, they just move on
+  const uint16_t* k_prev = nullptr;
+  const uint16_t* v_prev = nullptr;
+  const int64_t tile_elems = static_cast<int64_t>(kPfKeys) * row_elems;
   auto prepare = [&](int tt) {
     const int t0 = tt * kPfKeys;
+    char* kdst = lds.stage[tt & 1].k + wid * kBlockBytes;
+    char* vdst = lds.stage[tt & 1].v + wid * 4 * kBlockBytes;
+    // rows 8 wid .. 8 wid + 7 of tiles tt - 1 and tt in one page, none past kend
+    const bool same_page = tt > 0 && offw >= kPfKeys && offw + 7 < bsz && t0 + kPfKeys <= kend;
+    if (same_page) {
+      k_prev += tile_elems;
+      v_prev += tile_elems;
+      offw += kPfKeys;
+      if (offw >= bsz) {
+        offw -= bsz;
+        ++lpw;
+      }
+      return NextTile{k_prev, v_prev, kdst, vdst};
+    }
     if (lpw + 8 - win_base >= 64) {
       win_base = lpw;
       win = a.block_table[min(win_base + lane, nblocks - 1)];
@@ -215,14 +234,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
                            (static_cast<int64_t>(koff) * row_elems + g * kHeadSize + 8 * k_piece);
     const uint16_t* vsrc = a.v + vpage * a.v_page_stride +
                            (static_cast<int64_t>(voff) * row_elems + g * kHeadSize + 8 * v_piece);
-    PrefillStage& st = lds.stage[tt & 1];
+    k_prev = ksrc;
+    v_prev = vsrc;
     offw += step_off;
     lpw += step_pages;
     if (offw >= bsz) {
       offw -= bsz;
       ++lpw;
     }
-    return NextTile{ksrc, vsrc, st.k + wid * kBlockBytes, st.v + wid * 4 * kBlockBytes};
+    return NextTile{ksrc, vsrc, kdst, vdst};
   };
   // load i of a tile: K piece group i / 2 (even i) or V piece group i / 2 (odd i)
   auto load = [&](const NextTile& nt, int i) {
