@@ -92,13 +92,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast
 // Written as asm so the compiler does not order later LDS reads behind it:
 // the loop waits for these loads itself (vmcnt(0) before each barrier), and
 // they only ever fill the stage no wave is reading.
+// M0 (the LDS base of the load) is declared clobbered; clang warns that M0
+// is reserved, and no other code of this kernel uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)lds_dst)));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(dst));
+               : "v"(src), "s"(dst)
+               : "m0");
 }
+#pragma clang diagnostic pop
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {

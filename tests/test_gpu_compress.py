@@ -191,3 +191,23 @@ def test_compress_bad_indices_give_nan_rows_and_empty_is_noop():
     empty = to_dev(synth.build_compress_case("e", 1, 64, 64, block_size=8, seed=1,
                                              boundaries=[]))
     assert run(empty).shape == (0, 512)
+
+
+def test_compress_workspace_reused_across_calls():
+    # One caller-held workspace serves several calls, one of them with fewer
+    # outputs and parts: every call depends only on what it writes itself.
+    print("[gpu] compress workspace reuse", flush=True)
+    big = to_dev(synth.build_compress_case("wr", 2, 4096, 256, block_size=8, seed=31))
+    small = to_dev(synth.build_compress_case("ws", 1, 1024, 128, block_size=8, seed=32))
+    prm = pkv.compress_params(big.state_cache, big.token_to_req, big.boundaries,
+                              big.block_table, big.compress_ratio, 8)
+    ws = torch.empty(pkv.compress_workspace_bytes(prm), dtype=torch.uint8, device="cuda")
+    outs = []
+    for case, splits in ((big, 8), (big, 8), (small, 4), (big, 8)):
+        out = pkv.compress(case.state_cache, case.token_to_req, case.positions, case.boundaries,
+                           case.block_table, case.compress_ratio, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+    check(big, outs[0], what="first call")
+    check(small, outs[2], what="smaller call on the same workspace")
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[3])
