@@ -194,7 +194,9 @@ def measure_append(name, num_tokens, block_size, steps, warmup, torch, pkv, synt
         e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    res = {"workload": name, "kernel": "append_kernel", "tokens": num_tokens,
+    # the library moves two tokens per wave from 2048 tokens of 4 x 256 rows
+    kernel = "append_pairs_kernel" if num_tokens >= 2048 else "append_kernel"
+    res = {"workload": name, "kernel": kernel, "tokens": num_tokens,
            "block_size": block_size, "cold_copies": copies, "steps": steps,
            "algorithmic_bytes": nbytes, "us_per_append": round(us, 3),
            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),

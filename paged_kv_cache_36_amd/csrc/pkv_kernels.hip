@@ -1,5 +1,4 @@
-// HIP kernels for single-token decode attention over a paged KV cache, gfx950,
-// and the KV append.
+// HIP kernels for single-token decode attention over a paged KV cache, gfx950.
 //
 // Work split. With fixed partitions one workgroup (4 waves) owns one
 // (sequence, partition, KV head) triple, the KV head fastest in the grid so
@@ -908,52 +907,6 @@ hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// KV append: token b's K and V rows go to the cache row of slot slots[b]
-// (page = slot / B, offset = slot % B). One wave per token; a lane moves
-// 16-byte chunks, all of a token's loads issued before its stores. Padding
-// (negative) and out-of-cache slots write nothing.
-// ---------------------------------------------------------------------------
-constexpr int kAppendThreads = 256;
-constexpr int kAppendTokensPerBlock = kAppendThreads / 64;
-
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
-  const int lane = lane_id();
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * kAppendTokensPerBlock + wave_id();
-  if (b >= a.num_tokens) return;
-  const int64_t slot = a.slots[b];
-  if (slot < 0 || slot >= a.num_slots) return;
-  const int64_t page = slot / a.block_size;
-  const int64_t offset = slot - page * a.block_size;
-  const int64_t row_elems = static_cast<int64_t>(a.row_chunks) * 8;
-  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_new + b * a.k_new_stride);
-  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_new + b * a.v_new_stride);
-  u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache + page * a.k_page_stride + offset * row_elems);
-  u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache + page * a.v_page_stride + offset * row_elems);
-  // rows of up to 4 KiB in one pass (2 chunks per lane each for K and V)
-  int c = lane;
-  for (; c + 64 < a.row_chunks; c += 128) {
-    const u32x4 k0 = ks[c], k1 = ks[c + 64], v0 = vs[c], v1 = vs[c + 64];
-    kd[c] = k0;
-    kd[c + 64] = k1;
-    vd[c] = v0;
-    vd[c + 64] = v1;
-  }
-  if (c < a.row_chunks) {
-    const u32x4 k0 = ks[c], v0 = vs[c];
-    kd[c] = k0;
-    vd[c] = v0;
-  }
-}
-
-hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  if (a.num_tokens <= 0) return hipSuccess;
-  const int64_t blocks = (static_cast<int64_t>(a.num_tokens) + kAppendTokensPerBlock - 1) /
-                         kAppendTokensPerBlock;
-  hipLaunchKernelGGL(append_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kAppendThreads), 0,
-                     stream, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* offsets,
                                 hipStream_t stream) {
