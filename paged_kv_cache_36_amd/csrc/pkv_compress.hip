@@ -45,7 +45,9 @@ struct CmpLds {
   f32x4 num[2][64];
 };
 
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
 
 __global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArgs a) {
   __shared__ CmpLds lds;
