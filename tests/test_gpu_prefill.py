@@ -56,6 +56,9 @@ def check(case, q_new, out, out32, rows=None):
 @pytest.mark.parametrize("nq,length,bsz", [
     (2, 2, 64), (17, 40, 16), (128, 128, 832), (129, 300, 784), (200, 1000, 832),
     (1, 500, 64), (333, 333, 64), (64, 4097, 784),
+    # pages of 1, 5 and 100 tokens: page crossings inside a wave's rows and
+    # page-id window reloads (more than 64 pages per workgroup)
+    (70, 150, 1), (130, 1000, 5), (300, 2000, 100),
 ])
 def test_prefill_small_full_check(nq, length, bsz):
     print(f"[gpu] prefill Q={nq} L={length} B={bsz}", flush=True)
@@ -126,3 +129,27 @@ def test_prefill_other_scales(scale):
     case.scale = scale
     out, out32 = run_prefill(case, q_new)
     check(case, q_new, out, out32)
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 3])
+def test_prefill_other_kv_head_counts(hkv):
+    # 6 query heads per KV head for 1, 2 and 3 KV heads: the grid deals
+    # workgroups to XCDs by KV head when the head count divides 8, and in
+    # plain order otherwise (3)
+    print(f"[gpu] prefill Hkv={hkv}", flush=True)
+    nq, length, bsz = 300, 1500, 784
+    case, q_new = synth.build_prefill_case("pfh", nq, length, bsz, seed=50 + hkv, device="cuda")
+    kc = case.k_cache[:, :, :hkv].contiguous()
+    vc = case.v_cache[:, :, :hkv].contiguous()
+    q = q_new[:, : 6 * hkv].contiguous()
+    out32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    out, _ = pkv.prefill(q, kc, vc, case.block_table[0], length, bsz, case.scale, out_f32=out32)
+    torch.cuda.synchronize()
+    k = f64(case.keys(0))[:, :hkv]
+    v = f64(case.values(0))[:, :hkv]
+    ref, _ = opf.attention_prefill(f64(q), k, v, case.scale)
+    got32 = f64(out32)
+    for i in range(nq):
+        vmax = np.abs(v[: length - nq + i + 1]).max()
+        assert np.abs(got32[i] - ref[i]).max() <= 2.0 ** -8 * vmax, f"query {i}"
+    assert_bf16_close(out, ref, what=f"prefill Hkv={hkv}")
