@@ -222,10 +222,15 @@ def measure_prefill(name, steps, warmup, torch, pkv, synth):
     out = torch.empty_like(q_new)
     bt = case.block_table[0]
     stream = torch.cuda.Stream()
+    prm = pkv.prefill_params(q_new, case.k_cache, case.v_cache, bt, length, case.block_size,
+                             case.scale)
+    splits = pkv.prefill_key_splits(prm)
+    ws_bytes = pkv.prefill_workspace_bytes(prm)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
     def step(i):
         pkv.prefill(q_new, case.k_cache, case.v_cache, bt, length, case.block_size, case.scale,
-                    out=out)
+                    out=out, workspace=ws)
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -244,12 +249,14 @@ def measure_prefill(name, steps, warmup, torch, pkv, synth):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     tflops = flops / (us * 1e-6) / 1e12
-    res = {"workload": name, "kernel": "prefill_kernel", "num_q": nq, "seq_len": length,
-           "block_size": case.block_size, "steps": steps, "algorithmic_flops": flops,
+    kernel = "prefill_kernel" if splits == 1 else "prefill_kernel+prefill_combine_kernel"
+    res = {"workload": name, "kernel": kernel, "num_q": nq, "seq_len": length,
+           "block_size": case.block_size, "key_splits": splits, "steps": steps,
+           "algorithmic_flops": flops,
            "us_per_call": round(us, 2), "tflops": round(tflops, 1),
            "frac_peak_bf16_mfma": round(tflops / PEAK_BF16_TFLOPS, 4)}
     log(json.dumps(res))
-    del g, case, q_new, out
+    del g, case, q_new, out, ws
     torch.cuda.empty_cache()
     return res
 

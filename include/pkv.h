@@ -281,18 +281,37 @@ typedef struct {
   int32_t seq_len;            /* L: cached tokens incl. the new ones,
                                  Q <= L <= max_blocks * B                          */
   float scale;                /* softmax scale (1/16 for D = 256)                  */
+  int32_t key_splits;         /* 0: chosen by the library (pkv_prefill_key_splits);
+                                 1..64: each query block's keys cut into this many
+                                 ranges, merged by a second kernel (split-KV, the
+                                 same log-sum-exp merge as decode's partitions)    */
 } pkv_prefill_params;
+
+/* The key splits a pkv_prefill call with these params makes, or a negative
+ * pkv_status for invalid params. Host only. With key_splits = 0: one split
+ * while the launch has two or more workgroups per CU (128 queries x 1 head per
+ * workgroup, 256 CUs); else the smallest count that gives three, at most 16,
+ * keeping every split of the shortest query block at 16 or more 64-key tiles. */
+PKV_API int32_t pkv_prefill_key_splits(const pkv_prefill_params* params);
+/* Workspace pkv_prefill needs: 0 for one split, else splits * Q * Hq * (D + 1)
+ * * 4 bytes (fp32 partials and their log-sum-exps). 0 for invalid params. */
+PKV_API size_t pkv_prefill_workspace_bytes(const pkv_prefill_params* params);
 
 /* Device inputs: q bf16 [Q, Hq, D] contiguous; key_cache / value_cache as for
  * pkv_decode; block_table int32 [max_blocks] (this sequence's row). Device
  * outputs: out bf16 [Q, Hq, D] (RNE from fp32), out_f32 fp32 [Q, Hq, D] or
  * NULL (at least one of the two). p is rounded to bf16 for the P.V product
- * (fp32 accumulation). 16-byte aligned pointers; asynchronous on `stream`;
- * allocates nothing; host checks return an error before any launch. */
+ * (fp32 accumulation). workspace: caller-owned device memory of at least
+ * pkv_prefill_workspace_bytes(params) bytes, 16-byte aligned (may be NULL
+ * when that is 0); its contents need no initialization and are scratch after
+ * the call. 16-byte aligned pointers; asynchronous on `stream`; allocates
+ * nothing; host checks return an error before any launch (PKV_ERR_PARTITION
+ * for key_splits outside 0..64, PKV_ERR_WORKSPACE for a missing or short
+ * workspace). */
 PKV_API pkv_status pkv_prefill(const pkv_prefill_params* params, const void* q,
                                const void* key_cache, const void* value_cache,
                                const int32_t* block_table, void* out, float* out_f32,
-                               void* stream);
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Paged window compression ("From Attention to KV Cache Compression: Notes

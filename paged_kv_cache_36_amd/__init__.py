@@ -29,6 +29,9 @@ from .api import (  # noqa: F401
     page_tokens,
     plan,
     prefill,
+    prefill_key_splits,
+    prefill_params,
+    prefill_workspace_bytes,
     probe_copy,
     probe_read,
     split,

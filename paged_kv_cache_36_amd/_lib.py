@@ -72,6 +72,7 @@ class PrefillParams(ctypes.Structure):
         ("v_page_stride", ctypes.c_int64),
         ("seq_len", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("key_splits", ctypes.c_int32),
     ]
 
 
@@ -123,7 +124,10 @@ SIGNATURES = {
     "pkv_debug_gather": (_I32, [_P, _I32, _VP, _VP, _VP, _VP, _VP]),
     "pkv_append": (_I32, [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_page_tokens": (_I32, [ctypes.c_int64, ctypes.c_int64, _I32]),
-    "pkv_prefill": (_I32, [ctypes.POINTER(PrefillParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "pkv_prefill_key_splits": (_I32, [ctypes.POINTER(PrefillParams)]),
+    "pkv_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(PrefillParams)]),
+    "pkv_prefill": (_I32, [ctypes.POINTER(PrefillParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                           _VP]),
     "pkv_compress_splits": (_I32, [ctypes.POINTER(CompressParams)]),
     "pkv_compress_workspace_bytes": (_SZ, [ctypes.POINTER(CompressParams)]),
     "pkv_compress": (_I32, [ctypes.POINTER(CompressParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP,

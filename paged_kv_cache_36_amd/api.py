@@ -248,24 +248,11 @@ def append(k_new, v_new, slot_mapping, key_cache, value_cache, stream=None):
                              _ptr(key_cache), _ptr(value_cache), _stream(stream)), "pkv_append")
 
 
-def prefill(q, key_cache, value_cache, block_table, seq_len, block_size, scale, *, out=None,
-            out_f32=None, want_bf16=True, stream=None):
-    """Causal attention of one sequence's last q tokens (q: [Q, Hq, D] bf16)
-    over its seq_len cached tokens; returns (out, out_f32)."""
-    _need(q, "q", torch.bfloat16, 3)
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
-    k_stride = _page_stride(key_cache, "key_cache")
-    v_stride = _page_stride(value_cache, "value_cache")
-    _need(block_table, "block_table", torch.int32, 1)
-    if not block_table.is_contiguous():
-        raise ValueError("block_table must be contiguous")
+def prefill_params(q, key_cache, value_cache, block_table, seq_len, block_size, scale,
+                   key_splits=0):
+    """pkv_prefill_params for q [Q, Hq, D] over caches [pages, B, Hkv, D]."""
     nq, hq, d = q.shape
     _, bsz, hkv, _ = key_cache.shape
-    if bsz != block_size:
-        raise ValueError(f"block_size {block_size} does not match the cache ({bsz})")
-    if out is None and want_bf16:
-        out = torch.empty_like(q)
     p = PrefillParams()
     p.num_q_tokens = nq
     p.num_q_heads = hq
@@ -273,12 +260,52 @@ def prefill(q, key_cache, value_cache, block_table, seq_len, block_size, scale, 
     p.head_size = d
     p.block_size = block_size
     p.max_blocks = block_table.shape[0]
-    p.k_page_stride = k_stride
-    p.v_page_stride = v_stride
+    p.k_page_stride = _page_stride(key_cache, "key_cache")
+    p.v_page_stride = _page_stride(value_cache, "value_cache")
     p.seq_len = int(seq_len)
     p.scale = float(scale)
+    p.key_splits = int(key_splits)
+    return p
+
+
+def prefill_key_splits(params):
+    """The key splits pkv_prefill makes for these params (raises on invalid ones)."""
+    n = load().pkv_prefill_key_splits(ctypes.byref(params))
+    _check(min(n, 0), "pkv_prefill_key_splits")
+    return n
+
+
+def prefill_workspace_bytes(params):
+    """Workspace bytes pkv_prefill needs for these params (0 for one split)."""
+    return int(load().pkv_prefill_workspace_bytes(ctypes.byref(params)))
+
+
+def prefill(q, key_cache, value_cache, block_table, seq_len, block_size, scale, *, out=None,
+            out_f32=None, want_bf16=True, key_splits=0, workspace=None, stream=None):
+    """Causal attention of one sequence's last q tokens (q: [Q, Hq, D] bf16)
+    over its seq_len cached tokens; returns (out, out_f32). key_splits = 0
+    lets the library choose; the workspace is allocated with torch when the
+    call needs one and none is given."""
+    _need(q, "q", torch.bfloat16, 3)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _need(block_table, "block_table", torch.int32, 1)
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    bsz = key_cache.shape[1]
+    if bsz != block_size:
+        raise ValueError(f"block_size {block_size} does not match the cache ({bsz})")
+    if out is None and want_bf16:
+        out = torch.empty_like(q)
+    p = prefill_params(q, key_cache, value_cache, block_table, seq_len, block_size, scale,
+                       key_splits)
+    need = prefill_workspace_bytes(p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().pkv_prefill(ctypes.byref(p), _ptr(q), _ptr(key_cache), _ptr(value_cache),
-                              _ptr(block_table), _ptr(out), _ptr(out_f32), _stream(stream)),
+                              _ptr(block_table), _ptr(out), _ptr(out_f32), _ptr(workspace),
+                              ws_bytes, _stream(stream)),
            "pkv_prefill")
     return out, out_f32
 

@@ -196,6 +196,60 @@ void carve_workspace(const Plan& pl, void* workspace, pkv::LaunchArgs& a) {
 
 }  // namespace
 
+namespace {
+
+// Prefill key splits: queries per workgroup of the prefill kernel, the most
+// splits a call may ask for, and the CU count the automatic choice fills.
+constexpr int64_t kPrefillQueries = 128;
+constexpr int32_t kPrefillMaxSplits = 64;
+constexpr int64_t kCus = kPlanCUs;
+
+// Host checks shared by the prefill entry points.
+pkv_status check_prefill_params(const pkv_prefill_params* p) {
+  if (p->head_size != pkv::kHeadSize || p->num_kv_heads <= 0 ||
+      p->num_q_heads != pkv::kGroup * p->num_kv_heads)
+    return PKV_ERR_UNSUPPORTED;
+  if (p->block_size <= 0) return PKV_ERR_BLOCK_SIZE;
+  if (p->num_q_tokens < 1 || p->seq_len < p->num_q_tokens || p->max_blocks <= 0 ||
+      static_cast<int64_t>(p->seq_len) > static_cast<int64_t>(p->max_blocks) * p->block_size ||
+      !std::isfinite(p->scale))
+    return PKV_ERR_SHAPE;
+  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_size;
+  if (p->k_page_stride < p->block_size * row || p->v_page_stride < p->block_size * row ||
+      p->k_page_stride % 8 != 0 || p->v_page_stride % 8 != 0)
+    return PKV_ERR_STRIDE;
+  if (p->key_splits < 0 || p->key_splits > kPrefillMaxSplits) return PKV_ERR_PARTITION;
+  return PKV_OK;
+}
+
+// Key splits of a checked call: the caller's, else one while the launch
+// already has two workgroups per CU, else the smallest count giving three
+// (at most 16) that keeps 16 tiles in every split of the shortest block.
+// Measured on MI355X (Q = 1500, L = 20000, 288 workgroups unsplit): 1 / 2 /
+// 3 / 4 / 8 splits ran 1020 / 846 / 809 / 815 / 880 us; every split adds
+// partials and per-workgroup start-up, so a few rounds of workgroups are enough.
+int32_t prefill_key_splits(const pkv_prefill_params* p) {
+  if (p->key_splits > 0) return p->key_splits;
+  const int64_t nqb = (p->num_q_tokens + kPrefillQueries - 1) / kPrefillQueries;
+  const int64_t wgs = nqb * p->num_q_heads;
+  if (wgs >= 2 * kCus) return 1;
+  // keys of the shortest query block (block 0): up to its last query's position
+  const int64_t kend0 = static_cast<int64_t>(p->seq_len) - p->num_q_tokens +
+                        std::min<int64_t>(kPrefillQueries, p->num_q_tokens);
+  const int64_t tiles0 = (kend0 + 63) / 64;
+  int32_t k = 1;
+  while (k < 16 && wgs * k < 3 * kCus && tiles0 / (k + 1) >= 16) ++k;
+  return k;
+}
+
+size_t prefill_workspace(const pkv_prefill_params* p, int32_t splits) {
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(splits) * p->num_q_tokens * p->num_q_heads *
+         (pkv::kHeadSize + 1) * sizeof(float);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
@@ -471,27 +525,39 @@ pkv_status pkv_append(const pkv_append_params* p, const void* k_new, const void*
   return hip_status(pkv::launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pkv_prefill_key_splits(const pkv_prefill_params* p) {
+  if (!p) return PKV_ERR_NULL;
+  const pkv_status st = check_prefill_params(p);
+  if (st != PKV_OK) return st;
+  return prefill_key_splits(p);
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_prefill_params* p) {
+  if (!p || check_prefill_params(p) != PKV_OK) return 0;
+  return prefill_workspace(p, prefill_key_splits(p));
+}
+
 pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* key_cache,
                        const void* value_cache, const int32_t* block_table, void* out,
-                       float* out_f32, void* stream) {
+                       float* out_f32, void* workspace, size_t workspace_bytes, void* stream) {
   if (!p) return PKV_ERR_NULL;
-  if (p->head_size != pkv::kHeadSize || p->num_kv_heads <= 0 ||
-      p->num_q_heads != pkv::kGroup * p->num_kv_heads)
-    return PKV_ERR_UNSUPPORTED;
-  if (p->block_size <= 0) return PKV_ERR_BLOCK_SIZE;
-  if (p->num_q_tokens < 1 || p->seq_len < p->num_q_tokens || p->max_blocks <= 0 ||
-      static_cast<int64_t>(p->seq_len) > static_cast<int64_t>(p->max_blocks) * p->block_size ||
-      !std::isfinite(p->scale))
-    return PKV_ERR_SHAPE;
-  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_size;
-  if (p->k_page_stride < p->block_size * row || p->v_page_stride < p->block_size * row ||
-      p->k_page_stride % 8 != 0 || p->v_page_stride % 8 != 0)
-    return PKV_ERR_STRIDE;
+  const pkv_status st = check_prefill_params(p);
+  if (st != PKV_OK) return st;
   if (!q || !key_cache || !value_cache || !block_table || (!out && !out_f32) || !aligned(q, 16) ||
       !aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_table, 4) ||
       (out && !aligned(out, 16)) || (out_f32 && !aligned(out_f32, 16)))
     return PKV_ERR_NULL;
+  const int32_t splits = prefill_key_splits(p);
+  const size_t need = prefill_workspace(p, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return PKV_ERR_WORKSPACE;
   pkv::PrefillArgs a;
+  a.key_splits = splits;
+  a.o_part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.lse_part = need > 0 ? static_cast<float*>(workspace) +
+                              static_cast<int64_t>(splits) * p->num_q_tokens * p->num_q_heads *
+                                  pkv::kHeadSize
+                        : nullptr;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(key_cache);
   a.v = static_cast<const uint16_t*>(value_cache);

@@ -80,6 +80,12 @@ struct PrefillArgs {
   int32_t num_kv_heads;
   int32_t block_size;
   float scale_log2;             // scale * log2(e)
+  // key splits: 1 writes out / out_f32 directly; more write per-split partials
+  // (o_part fp32 [key_splits, num_q, Hq, D], lse_part fp32 [key_splits, num_q,
+  // Hq] in log2 units) that a second kernel merges into out / out_f32
+  int32_t key_splits;
+  float* o_part;
+  float* lse_part;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Paged window compression: per-dimension softmax over each boundary token's

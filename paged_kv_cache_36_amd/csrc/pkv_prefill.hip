@@ -26,6 +26,12 @@
 //    in that same key order.
 // At the end the two key halves of each query group merge through LDS.
 //
+// Key splits. When the query blocks are too few to fill the CUs, each block's
+// tiles are cut into key_splits near-equal ranges, one workgroup each; a
+// workgroup then writes its normalized partial output and log2-sum-exp, and
+// prefill_combine_kernel merges the splits with the same log-sum-exp weights
+// as decode's partitions (split-KV, flash-decoding style).
+//
 // LDS layout. A direct load writes 64 consecutive 16-byte slots; a tile is
 // stored as 1 KiB blocks of 8 rows x 8 pieces (128 contiguous bytes of each
 // row, so every load reads whole cache lines):
@@ -111,31 +117,40 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// (query head, query block) of workgroup b; false for grid padding. XCD x
-// serves KV head x % hkv, so one L2 sees every request for that head's tiles.
-__device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int& h, int& qb) {
-  const int per_kv = kGroup * nqb;
+// (query head, query block, key split) of workgroup b; false for grid
+// padding. XCD x serves KV head x % hkv, so one L2 sees every request for that
+// head's tiles. Query blocks go out longest first, the splits of one block
+// together.
+__device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int nsplit, int& h, int& qb,
+                                         int& split) {
+  const int per_kv = kGroup * nqb * nsplit;
+  int j;
   if (kXcds % hkv == 0) {
     const int x = b % kXcds;
-    const int j = (b / kXcds) * (kXcds / hkv) + x / hkv;
+    j = (b / kXcds) * (kXcds / hkv) + x / hkv;
     if (j >= per_kv) return false;
     h = (x % hkv) * kGroup + j % kGroup;
-    qb = nqb - 1 - j / kGroup;
-    return true;
+  } else {
+    const int hq = hkv * kGroup;
+    h = b % hq;
+    j = (b / hq) * kGroup;
   }
-  const int hq = hkv * kGroup;
-  h = b % hq;
-  qb = nqb - 1 - b / hq;
+  const int t = j / kGroup;
+  qb = nqb - 1 - t / nsplit;
+  split = t % nsplit;
   return true;
 }
 
-template <bool kFold>
+// kSplit: key_splits > 1 (partials out); with one split the tile range and
+// the grid decomposition fold to the plain whole-range form.
+template <bool kFold, bool kSplit>
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) PrefillLds lds;
   const int hq = a.num_kv_heads * kGroup;
   const int nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
-  int h, qb;
-  if (!block_of(blockIdx.x, a.num_kv_heads, nqb, h, qb)) return;
+  int h, qb, split;
+  const int nsplit = kSplit ? a.key_splits : 1;
+  if (!block_of(blockIdx.x, a.num_kv_heads, nqb, nsplit, h, qb, split)) return;
   const int g = h / kGroup;
   const int lane = lane_id();
   const int wid = wave_id();
@@ -151,6 +166,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int block_first = first_pos + q0;             // position of the block's first query
   const int kend = first_pos + min(q0 + kPfQueries, a.num_q);   // keys the block needs
   const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
+  // this workgroup's tiles: split `split` of key_splits near-equal ranges
+  const int t_lo = kSplit ? static_cast<int>(static_cast<int64_t>(ntiles) * split / nsplit) : 0;
+  const int t_hi =
+      kSplit ? static_cast<int>(static_cast<int64_t>(ntiles) * (split + 1) / nsplit) : ntiles;
   const int row_elems = a.num_kv_heads * kHeadSize;
   const int bsz = a.block_size;
 
@@ -176,13 +195,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int last_off = kend - 1 - last_lp * bsz;
   const int nblocks = (a.seq_len + bsz - 1) / bsz;
   const int64_t last_page = a.block_table[last_lp];
-  // logical page and offset of row 8 wid of the next tile to load
-  int lpw = (8 * wid) / bsz;
-  int offw = 8 * wid - lpw * bsz;
+  // logical page and offset of row 8 wid of the next tile to load (wave-uniform)
+  const int row0 = __builtin_amdgcn_readfirstlane(t_lo * kPfKeys + 8 * wid);
+  int lpw = row0 / bsz;
+  int offw = row0 - lpw * bsz;
   const int step_pages = kPfKeys / bsz, step_off = kPfKeys % bsz;
   // page ids of logical pages win_base .. win_base + 63, one per lane
-  int win_base = 0;
-  int win = a.block_table[min(lane, nblocks - 1)];
+  int win_base = lpw;
+  int win = a.block_table[min(win_base + lane, nblocks - 1)];
 
   // Source rows of the next tile's loads and the stage they fill; the eight
   // loads themselves are spread over the S^T products (load()), so no wave
@@ -203,7 +223,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     char* kdst = lds.stage[tt & 1].k + wid * kBlockBytes;
     char* vdst = lds.stage[tt & 1].v + wid * 4 * kBlockBytes;
     // rows 8 wid .. 8 wid + 7 of tiles tt - 1 and tt in one page, none past kend
-    const bool same_page = tt > 0 && offw >= kPfKeys && offw + 7 < bsz && t0 + kPfKeys <= kend;
+    const bool same_page = tt > t_lo && offw >= kPfKeys && offw + 7 < bsz && t0 + kPfKeys <= kend;
     if (same_page) {
       k_prev += tile_elems;
       v_prev += tile_elems;
@@ -370,14 +390,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   };
 
   // tiles whose 64 keys all precede the block's first query need no mask
-  const int n_open = min(ntiles, (block_first + 1) / kPfKeys);
+  const int n_open = min(t_hi, max(t_lo, (block_first + 1) / kPfKeys));
   {
-    const NextTile nt = prepare(0);
+    const NextTile nt = prepare(t_lo);
 #pragma unroll
     for (int i = 0; i < 8; ++i) load(nt, i);
   }
-  for (int tt = 0; tt < n_open; ++tt) step(tt, std::false_type{});
-  for (int tt = n_open; tt < ntiles; ++tt) step(tt, std::true_type{});
+  for (int tt = t_lo; tt < n_open; ++tt) step(tt, std::false_type{});
+  for (int tt = n_open; tt < t_hi; ++tt) step(tt, std::true_type{});
 
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the spare loads into LDS are done
   // The two key halves of a query group merge through LDS (the tiles are
@@ -396,10 +416,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
   if (kh == 1 || !q_valid) return;
+  // the max of both halves; -inf only when the query sees no key of this
+  // workgroup's split (with one split, key 0 is visible to every query)
+  float mx = fmaxf(m, mbuf[kPfCols * kHeadSize + lane]);
+  if (mx == -INFINITY) mx = 0.f;   // both halves empty: every weight stays 0
   {
     const float m2 = mbuf[kPfCols * kHeadSize + lane];
     const float l2 = mbuf[kPfCols * kHeadSize + 64 + lane];
-    const float mx = fmaxf(m, m2);   // finite: key 0 is visible to every query
     const float f1 = exp2_fast(m - mx), f2 = exp2_fast(m2 - mx);
     lsum = lsum * f1 + l2 * f2;
 #pragma unroll
@@ -407,8 +430,23 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * f1 + mbuf[(db * 16 + r) * 64 + lane] * f2;
   }
-  // o = acc / l: register r of block db holds dim 32 db + 8 (r / 4) + 4 half + r % 4
-  const float inv = 1.f / lsum;   // lsum >= 1: the maximum key has weight 1
+  // o = acc / l: register r of block db holds dim 32 db + 8 (r / 4) + 4 half + r % 4.
+  // One split: lsum >= 1 (the maximum key has weight 1). Several: the split's
+  // normalized partial and its log2-sum-exp, or 0 and -inf for no key.
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if constexpr (kSplit) {
+    const int64_t prow = (static_cast<int64_t>(split) * a.num_q + qi) * hq + h;
+    if (half == 0) a.lse_part[prow] = lsum > 0.f ? mx + __log2f(lsum) : -INFINITY;
+    float* orow = a.o_part + prow * kHeadSize + 4 * half;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * rq) =
+            f32x4{acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv, acc[db][4 * rq + 2] * inv,
+                  acc[db][4 * rq + 3] * inv};
+    return;
+  }
   const int64_t orow = (static_cast<int64_t>(qi) * hq + h) * kHeadSize + 4 * half;
 #pragma unroll
   for (int db = 0; db < 8; ++db)
@@ -427,24 +465,60 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// Merge of the key splits: one thread per (query, head, 4 dims);
+// o = sum_j 2^(lse_j - M) o_j / sum_j 2^(lse_j - M), M = max_j lse_j (split 0
+// holds key 0, so M is finite), then the bf16 (RNE) and fp32 outputs.
+constexpr int kPfCombineThreads = 256;
+
+__global__ __launch_bounds__(kPfCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
+  const int hq = a.num_kv_heads * kGroup;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPfCombineThreads + threadIdx.x;
+  const int64_t row = t / (kHeadSize / 4);   // query * hq + head
+  if (row >= static_cast<int64_t>(a.num_q) * hq) return;
+  const int d = static_cast<int>(t - row * (kHeadSize / 4)) * 4;
+  const int64_t split_rows = static_cast<int64_t>(a.num_q) * hq;
+  float mx = -INFINITY;
+  for (int j = 0; j < a.key_splits; ++j) mx = fmaxf(mx, a.lse_part[j * split_rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int j = 0; j < a.key_splits; ++j) {
+    const float w = exp2_fast(a.lse_part[j * split_rows + row] - mx);   // 0 for an empty split
+    den += w;
+    acc += w * *reinterpret_cast<const f32x4*>(a.o_part + (j * split_rows + row) * kHeadSize + d);
+  }
+  const f32x4 o = acc * (1.f / den);
+  const int64_t idx = row * kHeadSize + d;
+  if (a.out) {
+    u32x2 packed;
+    packed.x = f32_to_bf16(o.x) | (f32_to_bf16(o.y) << 16);
+    packed.y = f32_to_bf16(o.z) | (f32_to_bf16(o.w) << 16);
+    *reinterpret_cast<u32x2*>(a.out + idx) = packed;
+  }
+  if (a.out_f32) *reinterpret_cast<f32x4*>(a.out_f32 + idx) = o;
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_q <= 0) return hipSuccess;
   const int64_t nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
-  int64_t blocks = static_cast<int64_t>(a.num_kv_heads) * kGroup * nqb;
+  const int64_t per_kv = kGroup * nqb * a.key_splits;
+  int64_t blocks = static_cast<int64_t>(a.num_kv_heads) * per_kv;
   if (kXcds % a.num_kv_heads == 0) {
     // every XCD gets the same number of slots; slots past a head's list exit
-    const int64_t per_xcd =
-        (kGroup * nqb + kXcds / a.num_kv_heads - 1) / (kXcds / a.num_kv_heads);
+    const int64_t per_xcd = (per_kv + kXcds / a.num_kv_heads - 1) / (kXcds / a.num_kv_heads);
     blocks = per_xcd * kXcds;
   }
-  if (a.scale_log2 > 0.f)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads),
-                       0, stream, a);
+  const bool fold = a.scale_log2 > 0.f, split = a.key_splits > 1;
+  auto kernel = fold ? (split ? prefill_kernel<true, true> : prefill_kernel<true, false>)
+                     : (split ? prefill_kernel<false, true> : prefill_kernel<false, false>);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kPfThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.key_splits == 1) return e;
+  const int64_t threads = static_cast<int64_t>(a.num_q) * a.num_kv_heads * kGroup * (kHeadSize / 4);
+  hipLaunchKernelGGL(prefill_combine_kernel,
+                     dim3(static_cast<uint32_t>((threads + kPfCombineThreads - 1) / kPfCombineThreads)),
+                     dim3(kPfCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -303,3 +303,56 @@ def test_compress_workspace_and_argument_checks(lib):
                             None) == -5
     assert lib.pkv_compress(ctypes.byref(p), fake, fake, fake, fake, fake, fake, ctypes.c_void_p(16),
                             1 << 20, None) == -5                 # workspace not 256-byte aligned
+
+
+def prefill_params(**kw):
+    p = _lib.PrefillParams()
+    base = dict(num_q_tokens=1500, num_q_heads=24, num_kv_heads=4, head_size=256, block_size=832,
+                max_blocks=25, k_page_stride=832 * 1024, v_page_stride=832 * 1024,
+                seq_len=20000, scale=1.0 / 16, key_splits=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,splits", [
+    # 12 query blocks x 24 heads = 288 workgroups: 3 splits give 864 (3.4 per CU)
+    ({}, 3),
+    # 32 blocks x 24 heads = 768 workgroups already: one split
+    (dict(num_q_tokens=4096, seq_len=32768, max_blocks=40), 1),
+    # the shortest block has 2300 + 128 keys = 38 tiles: 2 splits keep 16 each
+    (dict(num_q_tokens=700, seq_len=3000, max_blocks=4), 2),
+    # one query over 32768 keys: 24 workgroups, 16 splits (the cap)
+    (dict(num_q_tokens=1, seq_len=32768, max_blocks=40), 16),
+    # too few tiles to split
+    (dict(num_q_tokens=200, seq_len=1000, max_blocks=2), 1),
+    # the caller's count
+    (dict(key_splits=7), 7),
+])
+def test_prefill_key_split_choice(lib, kw, splits):
+    p = prefill_params(**kw)
+    assert lib.pkv_prefill_key_splits(ctypes.byref(p)) == splits
+    need = lib.pkv_prefill_workspace_bytes(ctypes.byref(p))
+    expect = 0 if splits == 1 else splits * p.num_q_tokens * 24 * 257 * 4
+    assert need == expect
+
+
+def test_prefill_validates_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)
+    pf = lib.pkv_prefill
+    p = prefill_params()
+    need = lib.pkv_prefill_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert pf(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, 0, None) == -5
+    assert pf(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, need - 1, None) == -5
+    assert pf(ctypes.byref(p), fake, fake, fake, fake, fake, None, mis, need, None) == -5
+    assert pf(ctypes.byref(p), fake, fake, fake, fake, None, None, fake, need, None) == -1
+    for bad in (dict(key_splits=-1), dict(key_splits=65)):
+        q = prefill_params(**bad)
+        assert lib.pkv_prefill_key_splits(ctypes.byref(q)) == -4
+        assert lib.pkv_prefill_workspace_bytes(ctypes.byref(q)) == 0
+        assert pf(ctypes.byref(q), fake, fake, fake, fake, fake, None, fake, need, None) == -4
+    assert lib.pkv_prefill_key_splits(ctypes.byref(prefill_params(seq_len=100))) == -2
+    assert lib.pkv_prefill_key_splits(None) == -1

@@ -28,10 +28,11 @@ def _gpu():
     pkv.load()
 
 
-def run_prefill(case, q_new):
+def run_prefill(case, q_new, key_splits=0):
     out32 = torch.empty(q_new.shape, dtype=torch.float32, device="cuda")
     out, _ = pkv.prefill(q_new, case.k_cache, case.v_cache, case.block_table[0],
-                         case.lens[0], case.block_size, case.scale, out_f32=out32)
+                         case.lens[0], case.block_size, case.scale, out_f32=out32,
+                         key_splits=key_splits)
     torch.cuda.synchronize()
     return out, out32
 
@@ -153,3 +154,39 @@ def test_prefill_other_kv_head_counts(hkv):
         vmax = np.abs(v[: length - nq + i + 1]).max()
         assert np.abs(got32[i] - ref[i]).max() <= 2.0 ** -8 * vmax, f"query {i}"
     assert_bf16_close(out, ref, what=f"prefill Hkv={hkv}")
+
+
+@pytest.mark.parametrize("nq,length,bsz,splits,scale", [
+    # 11 tiles per query block: 2 and 3 splits; 7 puts the diagonal tiles in
+    # splits of their own (queries that see no key of a split); 64 leaves
+    # most splits empty
+    (130, 700, 64, 2, 1.0 / 16), (130, 700, 64, 3, 1.0 / 16), (130, 700, 64, 7, 1.0 / 16),
+    (130, 700, 64, 64, 1.0 / 16),
+    # the unfolded-scale instantiation, pages of 5 tokens
+    (200, 1500, 5, 5, -1.0 / 16),
+    # one query (the decode shape through prefill), 16 splits
+    (1, 5000, 832, 16, 1.0 / 16),
+])
+def test_prefill_forced_key_splits(nq, length, bsz, splits, scale):
+    print(f"[gpu] prefill Q={nq} L={length} B={bsz} splits={splits}", flush=True)
+    case, q_new = synth.build_prefill_case("pfk", nq, length, bsz, seed=7 * splits + nq,
+                                           device="cuda")
+    case.scale = scale
+    out, out32 = run_prefill(case, q_new, key_splits=splits)
+    check(case, q_new, out, out32)
+
+
+def test_prefill_auto_splits_match_one_split():
+    # the library's own choice (5 splits here) against one split: both within
+    # the oracle's tolerance, and close to each other at fp32
+    print("[gpu] prefill auto splits vs one split", flush=True)
+    case, q_new = synth.build_prefill_case("pfa", 600, 6000, 832, seed=77, device="cuda")
+    p = pkv.prefill_params(q_new, case.k_cache, case.v_cache, case.block_table[0], case.lens[0],
+                           case.block_size, case.scale)
+    assert pkv.prefill_key_splits(p) > 1
+    out_a, out32_a = run_prefill(case, q_new)
+    out_1, out32_1 = run_prefill(case, q_new, key_splits=1)
+    check(case, q_new, out_a, out32_a)
+    check(case, q_new, out_1, out32_1)
+    vmax = float(case.values(0).float().abs().max())
+    assert float((out32_a - out32_1).abs().max()) <= 2.0 ** -8 * vmax
