@@ -52,8 +52,10 @@ typedef enum {
   PKV_OK = 0,
   PKV_ERR_NULL = -1,        /* a required pointer is NULL or misaligned           */
   PKV_ERR_SHAPE = -2,       /* head counts / sizes / table width inconsistent     */
-  PKV_ERR_BLOCK_SIZE = -3,  /* block_size not a positive multiple of 16           */
-  PKV_ERR_PARTITION = -4,   /* partition_tokens not 0 and not a multiple of 64    */
+  PKV_ERR_BLOCK_SIZE = -3,  /* block_size not a positive multiple of 16 (decode;
+                               prefill and append accept any positive size)       */
+  PKV_ERR_PARTITION = -4,   /* partition_tokens not 0 and not a multiple of 64,
+                               or a prefill key_splits outside 0..64              */
   PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
   PKV_ERR_UNSUPPORTED = -6, /* head_size != 256, group size != 6, or the call does
                                not apply to this plan                             */

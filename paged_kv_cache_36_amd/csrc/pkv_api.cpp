@@ -259,9 +259,10 @@ const char* pkv_status_string(int status) {
     case PKV_OK: return "ok";
     case PKV_ERR_NULL: return "null or misaligned pointer";
     case PKV_ERR_SHAPE: return "inconsistent shape";
-    case PKV_ERR_BLOCK_SIZE: return "block_size must be a positive multiple of 16";
-    case PKV_ERR_PARTITION: return "partition_tokens must be 0 or a multiple of 64";
-    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_BLOCK_SIZE: return "block_size must be positive (a multiple of 16 for decode)";
+    case PKV_ERR_PARTITION:
+      return "partition_tokens must be 0 or a multiple of 64 (prefill: key_splits 0..64)";
+    case PKV_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case PKV_ERR_UNSUPPORTED: return "unsupported head geometry (need head_size 256, 6 query heads per KV head)";
     case PKV_ERR_HIP: return "HIP launch or runtime error";
     case PKV_ERR_STRIDE: return "page stride smaller than a page or not a multiple of 8";
