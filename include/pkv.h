@@ -346,7 +346,9 @@ typedef struct {
 } pkv_compress_params;
 
 /* Window parts per output the library would use (num_splits resolved), or a
- * negative pkv_status for invalid params. Host only. */
+ * negative pkv_status for invalid params. Host only. With num_splits = 0: the
+ * smallest power of two giving num_outputs * S >= 256 workgroups (one per CU)
+ * while parts keep 16 or more rows, raised as needed to the 64-block limit. */
 PKV_API int32_t pkv_compress_splits(const pkv_compress_params* params);
 
 /* Device workspace bytes pkv_compress needs (0 when one part covers each

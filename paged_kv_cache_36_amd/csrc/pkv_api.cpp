@@ -580,10 +580,16 @@ pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* k
 namespace {
 
 // Window parts per output: the caller's S, else the smallest power of two that
-// gives at least 1024 workgroups while parts keep 16 rows or more. Every part
+// gives at least one workgroup per CU (256) while parts keep 16 rows or more.
+// Measured on MI355X over the 12 shapes (1/4/8 requests, C = 128/256/512):
+// more parts than that only add partials and the combine launch (4 x 32768
+// tokens, C = 128: 1 / 2 / 4 parts ran 24.6 / 29.2 / 32.2 us), and a target of
+// 1024 workgroups was up to 24 % slower on every shape it split. Every part
 // must touch at most kCompressMaxBlocks logical blocks (its ids sit one per
 // lane), and an output has at most kCompressMaxSplits parts (the combine's
 // lanes). Returns a negative status for invalid params.
+constexpr int64_t kCompressTargetWorkgroups = 256;
+
 int32_t compress_splits(const pkv_compress_params* p) {
   if (!p) return PKV_ERR_NULL;
   if (p->head_dim != pkv::kCompressDim) return PKV_ERR_UNSUPPORTED;
@@ -608,7 +614,8 @@ int32_t compress_splits(const pkv_compress_params* p) {
   } else {
     s = 1;
     while (blocks_touched(s) > pkv::kCompressMaxBlocks) s *= 2;
-    while (static_cast<int64_t>(p->num_outputs) * s < 1024 && (c + 2 * s - 1) / (2 * s) >= 16)
+    while (static_cast<int64_t>(p->num_outputs) * s < kCompressTargetWorkgroups &&
+           (c + 2 * s - 1) / (2 * s) >= 16)
       s *= 2;
     if (s > c) s = c;
     if (s > pkv::kCompressMaxSplits) return PKV_ERR_UNSUPPORTED;

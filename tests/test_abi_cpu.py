@@ -267,11 +267,13 @@ def cparams(**kw):
 
 def test_compress_splits_auto_and_limits(lib):
     splits = lambda **kw: lib.pkv_compress_splits(ctypes.byref(cparams(**kw)))
-    # smallest power of two reaching 1024 workgroups while parts keep >= 16 rows
-    assert splits() == 8                                   # 64 outputs x 8 parts of 16 rows
-    assert splits(num_outputs=1024) == 1
-    assert splits(num_outputs=256, compress_ratio=512) == 4
-    assert splits(num_outputs=16, compress_ratio=512) == 32
+    # smallest power of two reaching 256 workgroups (one per CU) while parts
+    # keep >= 16 rows
+    assert splits() == 4                                   # 64 outputs x 4 parts of 32 rows
+    assert splits(num_outputs=256) == 1
+    assert splits(num_outputs=128, compress_ratio=256) == 2
+    assert splits(num_outputs=256, compress_ratio=512) == 2    # one 512-row part: 65 blocks
+    assert splits(num_outputs=16, compress_ratio=512) == 16
     assert splits(num_outputs=4096, compress_ratio=512) == 2   # a 512-row part touches 65 blocks
     assert splits(block_size=1, num_outputs=5) == 8            # parts of at most 63 one-row blocks
     assert splits(num_splits=3) == 3
@@ -290,7 +292,7 @@ def test_compress_splits_auto_and_limits(lib):
 
 def test_compress_workspace_and_argument_checks(lib):
     p = cparams()
-    assert lib.pkv_compress_workspace_bytes(ctypes.byref(p)) == 2 * 64 * 8 * 512 * 4
+    assert lib.pkv_compress_workspace_bytes(ctypes.byref(p)) == 2 * 64 * 4 * 512 * 4   # 4 parts
     assert lib.pkv_compress_workspace_bytes(ctypes.byref(cparams(num_outputs=1024))) == 0
     assert lib.pkv_compress_workspace_bytes(ctypes.byref(cparams(head_dim=7))) == 0
     fake = ctypes.c_void_p(256)
