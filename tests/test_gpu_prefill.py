@@ -132,19 +132,21 @@ def test_prefill_other_scales(scale):
     check(case, q_new, out, out32)
 
 
+@pytest.mark.parametrize("splits", [0, 3])
 @pytest.mark.parametrize("hkv", [1, 2, 3])
-def test_prefill_other_kv_head_counts(hkv):
+def test_prefill_other_kv_head_counts(hkv, splits):
     # 6 query heads per KV head for 1, 2 and 3 KV heads: the grid deals
     # workgroups to XCDs by KV head when the head count divides 8, and in
-    # plain order otherwise (3)
-    print(f"[gpu] prefill Hkv={hkv}", flush=True)
+    # plain order otherwise (3); with one split and with three
+    print(f"[gpu] prefill Hkv={hkv} splits={splits}", flush=True)
     nq, length, bsz = 300, 1500, 784
     case, q_new = synth.build_prefill_case("pfh", nq, length, bsz, seed=50 + hkv, device="cuda")
     kc = case.k_cache[:, :, :hkv].contiguous()
     vc = case.v_cache[:, :, :hkv].contiguous()
     q = q_new[:, : 6 * hkv].contiguous()
     out32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    out, _ = pkv.prefill(q, kc, vc, case.block_table[0], length, bsz, case.scale, out_f32=out32)
+    out, _ = pkv.prefill(q, kc, vc, case.block_table[0], length, bsz, case.scale, out_f32=out32,
+                         key_splits=splits)
     torch.cuda.synchronize()
     k = f64(case.keys(0))[:, :hkv]
     v = f64(case.values(0))[:, :hkv]
