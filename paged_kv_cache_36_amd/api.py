@@ -399,19 +399,25 @@ def compress_finalize(compressed, positions, boundary_token_indices, rms_norm_we
         raise ValueError("compressed [N, 512], rms_norm_weight [512], cos_sin_cache [rows, 64]")
     if kv_slot_mapping.shape[0] != positions.shape[0]:
         raise ValueError("kv_slot_mapping and positions differ in length")
+    p = _finalize_params(compressed.shape[0], positions, cos_sin_cache, kv_cache,
+                         compress_ratio, rms_norm_eps)
+    _check(load().pkv_compress_finalize(ctypes.byref(p), _ptr(compressed), _ptr(positions),
+                                        _ptr(boundary_token_indices), _ptr(rms_norm_weight),
+                                        _ptr(cos_sin_cache), _ptr(kv_slot_mapping), _ptr(kv_cache),
+                                        _stream(stream)), "pkv_compress_finalize")
+    return kv_cache
+
+
+def _finalize_params(n, positions, cos_sin_cache, kv_cache, compress_ratio, rms_norm_eps):
     p = FinalizeParams()
-    p.num_outputs = compressed.shape[0]
+    p.num_outputs = n
     p.num_tokens = positions.shape[0]
     p.compress_ratio = int(compress_ratio)
     p.cos_sin_rows = cos_sin_cache.shape[0]
     p.num_kv_pages = kv_cache.shape[0]
     p.kv_page_stride = kv_cache.stride(0)
     p.rms_norm_eps = float(rms_norm_eps)
-    _check(load().pkv_compress_finalize(ctypes.byref(p), _ptr(compressed), _ptr(positions),
-                                        _ptr(boundary_token_indices), _ptr(rms_norm_weight),
-                                        _ptr(cos_sin_cache), _ptr(kv_slot_mapping), _ptr(kv_cache),
-                                        _stream(stream)), "pkv_compress_finalize")
-    return kv_cache
+    return p
 
 
 def page_tokens(state_page_bytes: int, attn_bytes_per_token: int, alignment_tokens: int) -> int:

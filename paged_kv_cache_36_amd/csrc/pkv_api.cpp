@@ -624,6 +624,82 @@ int32_t compress_splits(const pkv_compress_params* p) {
   return static_cast<int32_t>(s);
 }
 
+// Launch arguments of a checked compression call with s parts; the workspace
+// (need bytes, s > 1) holds the parts' outputs, then their log2-sum-exps.
+pkv::CompressArgs compress_args(const pkv_compress_params* p, int32_t s, const float* state_cache,
+                                const int32_t* token_to_req, const int64_t* positions,
+                                const int64_t* boundary_token_indices, const int32_t* block_table,
+                                float* compressed, void* workspace, size_t need) {
+  pkv::CompressArgs a;
+  a.state = state_cache;
+  a.token_to_req = token_to_req;
+  a.positions = positions;
+  a.boundaries = boundary_token_indices;
+  a.block_table = block_table;
+  a.out = compressed;
+  a.o_part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.lse_part = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2)
+                        : nullptr;
+  a.block_stride = p->block_stride;
+  a.row_stride = p->row_stride;
+  a.num_outputs = p->num_outputs;
+  a.num_tokens = p->num_tokens;
+  a.num_reqs = p->num_reqs;
+  a.max_blocks = p->max_blocks;
+  a.block_size = p->block_size;
+  a.compress_ratio = p->compress_ratio;
+  a.num_splits = s;
+  a.part_rows = (p->compress_ratio + s - 1) / s;
+  a.combine_lanes = 1;
+  while (a.combine_lanes * 8 < s) a.combine_lanes *= 2;
+  return a;
+}
+
+pkv_status check_finalize_params(const pkv_finalize_params* p) {
+  if (p->num_outputs < 0 || p->num_tokens < 0 || p->compress_ratio < 1 || p->cos_sin_rows < 0 ||
+      p->num_kv_pages < 0 || (p->num_outputs > 0 && p->num_tokens < 1) ||
+      !std::isfinite(p->rms_norm_eps) || p->rms_norm_eps < 0.f ||
+      p->num_kv_pages > INT64_MAX / (pkv::kKvBlockSize * 2))
+    return PKV_ERR_SHAPE;
+  if (p->kv_page_stride < pkv::kKvBlockSize * (pkv::kKvTokenStride + pkv::kKvScaleDim) ||
+      p->kv_page_stride % 16 != 0)
+    return PKV_ERR_STRIDE;
+  return PKV_OK;
+}
+
+bool finalize_pointers_ok(const int64_t* positions, const int64_t* boundary_token_indices,
+                          const float* rms_norm_weight, const float* cos_sin_cache,
+                          const int64_t* kv_slot_mapping, const void* kv_cache) {
+  return positions && boundary_token_indices && rms_norm_weight && cos_sin_cache &&
+         kv_slot_mapping && kv_cache && aligned(rms_norm_weight, 16) &&
+         aligned(cos_sin_cache, 16) && aligned(kv_cache, 16) && aligned(positions, 8) &&
+         aligned(boundary_token_indices, 8) && aligned(kv_slot_mapping, 8);
+}
+
+// Finalizer arguments of a checked call; c comes from `compressed` unless the
+// caller sets the parts fields.
+pkv::FinalizeArgs finalize_args(const pkv_finalize_params* p, const int64_t* positions,
+                                const int64_t* boundary_token_indices, const float* rms_norm_weight,
+                                const float* cos_sin_cache, const int64_t* kv_slot_mapping,
+                                void* kv_cache) {
+  pkv::FinalizeArgs a;
+  a.compressed = nullptr;
+  a.positions = positions;
+  a.boundaries = boundary_token_indices;
+  a.weight = rms_norm_weight;
+  a.cos_sin = cos_sin_cache;
+  a.slots = kv_slot_mapping;
+  a.kv = static_cast<uint8_t*>(kv_cache);
+  a.num_kv_pages = p->num_kv_pages;
+  a.kv_page_stride = p->kv_page_stride;
+  a.num_outputs = p->num_outputs;
+  a.num_tokens = p->num_tokens;
+  a.compress_ratio = p->compress_ratio;
+  a.cos_sin_rows = p->cos_sin_rows;
+  a.eps = p->rms_norm_eps;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -653,28 +729,9 @@ pkv_status pkv_compress(const pkv_compress_params* p, const float* state_cache,
   const size_t need = pkv_compress_workspace_bytes(p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
     return PKV_ERR_WORKSPACE;
-  pkv::CompressArgs a;
-  a.state = state_cache;
-  a.token_to_req = token_to_req;
-  a.positions = positions;
-  a.boundaries = boundary_token_indices;
-  a.block_table = block_table;
-  a.out = compressed;
-  a.o_part = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.lse_part = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2)
-                        : nullptr;
-  a.block_stride = p->block_stride;
-  a.row_stride = p->row_stride;
-  a.num_outputs = p->num_outputs;
-  a.num_tokens = p->num_tokens;
-  a.num_reqs = p->num_reqs;
-  a.max_blocks = p->max_blocks;
-  a.block_size = p->block_size;
-  a.compress_ratio = p->compress_ratio;
-  a.num_splits = s;
-  a.part_rows = (p->compress_ratio + s - 1) / s;
-  a.combine_lanes = 1;
-  while (a.combine_lanes * 8 < s) a.combine_lanes *= 2;
+  const pkv::CompressArgs a = compress_args(p, s, state_cache, token_to_req, positions,
+                                            boundary_token_indices, block_table, compressed,
+                                            workspace, need);
   return hip_status(pkv::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -683,36 +740,15 @@ pkv_status pkv_compress_finalize(const pkv_finalize_params* p, const float* comp
                                  const float* rms_norm_weight, const float* cos_sin_cache,
                                  const int64_t* kv_slot_mapping, void* kv_cache, void* stream) {
   if (!p) return PKV_ERR_NULL;
-  if (p->num_outputs < 0 || p->num_tokens < 0 || p->compress_ratio < 1 || p->cos_sin_rows < 0 ||
-      p->num_kv_pages < 0 || (p->num_outputs > 0 && p->num_tokens < 1) ||
-      !std::isfinite(p->rms_norm_eps) || p->rms_norm_eps < 0.f ||
-      p->num_kv_pages > INT64_MAX / (pkv::kKvBlockSize * 2))
-    return PKV_ERR_SHAPE;
-  if (p->kv_page_stride < pkv::kKvBlockSize * (pkv::kKvTokenStride + pkv::kKvScaleDim) ||
-      p->kv_page_stride % 16 != 0)
-    return PKV_ERR_STRIDE;
-  if (p->num_outputs == 0) return PKV_OK;
-  if (!compressed || !positions || !boundary_token_indices || !rms_norm_weight ||
-      !cos_sin_cache || !kv_slot_mapping || !kv_cache || !aligned(compressed, 16) ||
-      !aligned(rms_norm_weight, 16) || !aligned(cos_sin_cache, 16) || !aligned(kv_cache, 16) ||
-      !aligned(positions, 8) || !aligned(boundary_token_indices, 8) ||
-      !aligned(kv_slot_mapping, 8))
+  const pkv_status st = check_finalize_params(p);
+  if (st != PKV_OK || p->num_outputs == 0) return st;
+  if (!compressed || !aligned(compressed, 16) ||
+      !finalize_pointers_ok(positions, boundary_token_indices, rms_norm_weight, cos_sin_cache,
+                            kv_slot_mapping, kv_cache))
     return PKV_ERR_NULL;
-  pkv::FinalizeArgs a;
+  pkv::FinalizeArgs a = finalize_args(p, positions, boundary_token_indices, rms_norm_weight,
+                                      cos_sin_cache, kv_slot_mapping, kv_cache);
   a.compressed = compressed;
-  a.positions = positions;
-  a.boundaries = boundary_token_indices;
-  a.weight = rms_norm_weight;
-  a.cos_sin = cos_sin_cache;
-  a.slots = kv_slot_mapping;
-  a.kv = static_cast<uint8_t*>(kv_cache);
-  a.num_kv_pages = p->num_kv_pages;
-  a.kv_page_stride = p->kv_page_stride;
-  a.num_outputs = p->num_outputs;
-  a.num_tokens = p->num_tokens;
-  a.compress_ratio = p->compress_ratio;
-  a.cos_sin_rows = p->cos_sin_rows;
-  a.eps = p->rms_norm_eps;
   return hip_status(pkv::launch_finalize(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -235,8 +235,9 @@ __device__ __forceinline__ void cmb_merge(CmbState& x, const f32x4& m2, const f3
     const float mref = mt == -INFINITY ? 0.f : mt;
     const float w1 = exp2_fast(x.m[d] - mref);
     const float w2 = exp2_fast(m2[d] - mref);
-    x.tot[d] = x.tot[d] * w1 + t2[d] * w2;
-    x.acc[d] = x.acc[d] * w1 + a2[d] * w2;
+    // explicit fma: one rounding order, whatever the compiler contracts
+    x.tot[d] = __builtin_fmaf(x.tot[d], w1, t2[d] * w2);
+    x.acc[d] = __builtin_fmaf(x.acc[d], w1, a2[d] * w2);
     x.m[d] = mt;
   }
 }
@@ -252,25 +253,20 @@ __device__ __forceinline__ f32x4 shfl_xor4(const f32x4& v, int mask) {
 // c = sum_p 2^(lse_p - LSE) c_p / sum_p 2^(lse_p - LSE).
 constexpr int kCmbPartsPerLane = 8;
 
-__global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressArgs a) {
-  const int g_lanes = a.combine_lanes;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCmpThreads + threadIdx.x;
-  const int64_t group = t / g_lanes;                  // (output, 4-dim group)
-  const int pg = static_cast<int>(t - group * g_lanes);
-  const int groups_per_out = kCompressDim / 4;
-  const bool live = group < static_cast<int64_t>(a.num_outputs) * groups_per_out;
-  const int64_t n = live ? group / groups_per_out : 0;
-  const int dim = static_cast<int>(group - n * groups_per_out) * 4;
-  const int64_t base = n * a.num_splits * kCompressDim + dim;
+// Lane g of the combine's merge for one (output, 4 dims): parts 8 g .. 8 g + 7
+// in turn (parts past num_splits merge as empty), from base (the output's
+// part 0 at these dims).
+__device__ __forceinline__ CmbState cmb_lane(const float* lse_part, const float* o_part,
+                                             int64_t base, int g, int num_splits) {
   f32x4 l[kCmbPartsPerLane], o[kCmbPartsPerLane];
 #pragma unroll
   for (int i = 0; i < kCmbPartsPerLane; ++i) {
-    const int j = pg * kCmbPartsPerLane + i;
+    const int j = g * kCmbPartsPerLane + i;
     l[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (live && j < a.num_splits) {
-      l[i] = *reinterpret_cast<const f32x4*>(a.lse_part + base + static_cast<int64_t>(j) * kCompressDim);
-      o[i] = *reinterpret_cast<const f32x4*>(a.o_part + base + static_cast<int64_t>(j) * kCompressDim);
+    if (j < num_splits) {
+      l[i] = *reinterpret_cast<const f32x4*>(lse_part + base + static_cast<int64_t>(j) * kCompressDim);
+      o[i] = *reinterpret_cast<const f32x4*>(o_part + base + static_cast<int64_t>(j) * kCompressDim);
     }
   }
   CmbState x;
@@ -287,15 +283,35 @@ __global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressA
       if (l[i][d] == -INFINITY) w[d] = 0.f;
     cmb_merge(x, l[i], w, o[i] * w);
   }
-  for (int mask = 1; mask < g_lanes; mask <<= 1)   // uniform trip count
-    cmb_merge(x, shfl_xor4(x.m, mask), shfl_xor4(x.tot, mask), shfl_xor4(x.acc, mask));
-  if (!live || pg != 0) return;
+  return x;
+}
+
+__device__ __forceinline__ f32x4 cmb_value(const CmbState& x) {
   f32x4 c;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     c[d] = x.tot[d] > 0.f ? x.acc[d] / x.tot[d] : 0.f;
     if (x.tot[d] != x.tot[d] || x.m[d] == INFINITY) c[d] = __builtin_nanf("");
   }
+  return c;
+}
+
+__global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressArgs a) {
+  const int g_lanes = a.combine_lanes;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kCmpThreads + threadIdx.x;
+  const int64_t group = t / g_lanes;                  // (output, 4-dim group)
+  const int pg = static_cast<int>(t - group * g_lanes);
+  const int groups_per_out = kCompressDim / 4;
+  const bool live = group < static_cast<int64_t>(a.num_outputs) * groups_per_out;
+  const int64_t n = live ? group / groups_per_out : 0;
+  const int dim = static_cast<int>(group - n * groups_per_out) * 4;
+  const int64_t base = n * a.num_splits * kCompressDim + dim;
+  CmbState x = cmb_lane(a.lse_part, a.o_part, live ? base : 0, live ? pg : a.num_splits,
+                        a.num_splits);
+  for (int mask = 1; mask < g_lanes; mask <<= 1)   // uniform trip count
+    cmb_merge(x, shfl_xor4(x.m, mask), shfl_xor4(x.tot, mask), shfl_xor4(x.acc, mask));
+  if (!live || pg != 0) return;
+  const f32x4 c = cmb_value(x);
   *reinterpret_cast<f32x4*>(a.out + n * kCompressDim + dim) = c;
 }
 
