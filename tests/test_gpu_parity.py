@@ -94,7 +94,9 @@ def test_tiny_workload():
         assert_bf16_close(run_decode(case, ptok), ref, what=f"tiny P={ptok}")
 
 
-@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
+# page sizes of the study (784, 832), the smallest (16), and other multiples of
+# 16 whose pages split the 64-token tiles differently (48, 80, 1024)
+@pytest.mark.parametrize("bsz", [16, 48, 64, 80, 784, 832, 1024])
 def test_length_sweep(bsz):
     case = synth.build_case(f"sweep{bsz}", lens=SWEEP_LENS, block_size=bsz, seed=21,
                             device="cuda")
