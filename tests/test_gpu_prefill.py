@@ -192,3 +192,20 @@ def test_prefill_auto_splits_match_one_split():
     check(case, q_new, out_1, out32_1)
     vmax = float(case.values(0).float().abs().max())
     assert float((out32_a - out32_1).abs().max()) <= 2.0 ** -8 * vmax
+
+
+def test_prefill_unbind_view_matches_separate_caches():
+    # K and V as the two halves of one [pages, 2, B, Hkv, D] tensor (page
+    # strides of 2 B Hkv D elements): the same result, bit for bit
+    print("[gpu] prefill unbind view", flush=True)
+    case, q_new = synth.build_prefill_case("pfu", 200, 2600, 832, seed=91, device="cuda")
+    joint = torch.stack([case.k_cache, case.v_cache], dim=1)
+    kc, vc = joint.unbind(1)
+    assert kc.stride(0) == 2 * case.k_cache.stride(0)
+    out_a, out32_a = run_prefill(case, q_new)
+    out32_b = torch.empty_like(out32_a)
+    out_b, _ = pkv.prefill(q_new, kc, vc, case.block_table[0], case.lens[0], case.block_size,
+                           case.scale, out_f32=out32_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_b), bits(out_a))
+    assert torch.equal(out32_b.view(torch.int32), out32_a.view(torch.int32))
