@@ -31,8 +31,11 @@ def run_append(pool_k, pool_v, rows_k, rows_v, slots):
     torch.cuda.synchronize()
 
 
+# N >= 2048 takes the two-tokens-per-wave kernel: even and odd counts (a last
+# wave with one token), pages of 100 tokens
 @pytest.mark.parametrize("bsz,n,pages", [(16, 1, 4), (64, 63, 4), (784, 64, 3), (832, 65, 3),
-                                         (832, 1000, 4), (64, 4096, 80)])
+                                         (832, 1000, 4), (64, 4096, 80), (832, 2049, 4),
+                                         (100, 3001, 40)])
 def test_append_bit_exact(bsz, n, pages):
     print(f"[gpu] append B={bsz} N={n} pages={pages}", flush=True)
     pk, rk, slots = synth.append_inputs(n, bsz, pages, seed=100 + n, pad_every=5 if n > 4 else 0,
