@@ -77,6 +77,7 @@ __all__ = [
     "quant_exponent",
     "quantize_nope",
     "rope_gptj",
+    "rope_position",
     "slot_byte_offsets",
     "finalize_output",
     "finalize_outputs",
@@ -295,6 +296,15 @@ def rope_gptj(y, cos, sin):
     return out
 
 
+def rope_position(p, compress_ratio):
+    """The cos/sin cache row of an output whose boundary token sits at
+    position p: the compressed position p_c = floor(p / C) * C, the start of
+    the C-token chunk holding p ([Attn→KV notes, "How One Output Is
+    Produced", the RoPE step])."""
+    c = int(compress_ratio)
+    return (int(p) // c) * c
+
+
 def slot_byte_offsets(slot):
     """(page, payload byte offset, scale byte offset) of a KV slot inside its
     page: page = slot // 64, payload at (slot % 64) * 576, scale at
@@ -325,15 +335,14 @@ def finalize_outputs(compressed, weight, eps, cos_sin_cache, positions, compress
     """Write every output's packed bytes into a copy of kv_cache (uint8
     [pages, page_bytes]): payload and scale at the slot's offsets. A negative
     slot, or one past the cache, writes nothing. positions[j] is output j's
-    boundary position p; its RoPE row is cos_sin_cache[(p // C) * C]."""
+    boundary position p; its RoPE row is cos_sin_cache[rope_position(p, C)]."""
     kv = np.array(kv_cache, dtype=np.uint8, copy=True)
     pages = kv.shape[0]
     for j, slot in enumerate(slots):
         slot = int(slot)
         if slot < 0 or slot >= pages * KV_BLOCK_SIZE:
             continue
-        p = int(positions[j])
-        pc = (p // int(compress_ratio)) * int(compress_ratio)
+        pc = rope_position(positions[j], compress_ratio)
         payload, scale, _ = finalize_output(compressed[j], weight, eps, cos_sin_cache[pc])
         page, po, so = slot_byte_offsets(slot)
         kv[page, po:po + TOKEN_STRIDE] = payload

@@ -121,8 +121,7 @@ def run_case(n_out, c_scale, eps, n_pages, seed, slots=None, pc_rows=600, c=128)
     for j in range(n_out):
         b = int(bnd[j])
         s = int(slots[b])
-        p = int(positions[b])
-        pc = (p // c) * c
+        pc = oc.rope_position(positions[b], c)
         if s < 0 or s >= n_pages * 64 or pc >= pc_rows:
             continue
         page, po, so = oc.slot_byte_offsets(s)
@@ -142,8 +141,11 @@ def run_case(n_out, c_scale, eps, n_pages, seed, slots=None, pc_rows=600, c=128)
 def test_finalize_bytes(n_out, c_scale, eps, seed):
     print(f"[gpu] finalize N={n_out} scale={c_scale} eps={eps}", flush=True)
     checked, alt = run_case(n_out, c_scale, eps, n_pages=max(8, n_out // 16 + 4), seed=seed)
+    cap = max(3, checked * 512 // 500)
+    print(f"[gpu] finalize N={n_out}: {alt} admissible non-nearest values of {checked * 512} "
+          f"checked (cap {cap})", flush=True)
     assert checked == n_out
-    assert alt <= max(3, checked * 512 // 500), f"{alt} alternative roundings in {checked} outputs"
+    assert alt <= cap, f"{alt} alternative roundings in {checked} outputs"
 
 
 def test_finalize_skips_bad_slots_indices_and_rows():
@@ -204,7 +206,10 @@ def test_compress_then_finalize_end_to_end():
     for j in range(n):
         b = int(case.boundaries[j])
         page, po, so = oc.slot_byte_offsets(int(slots[b]))
-        pc = (int(case.positions[b]) // 512) * 512
+        pc = oc.rope_position(case.positions[b], 512)
         alt += check_output(out[page, po:po + 576], out[page, so:so + 8], comp64[j],
                             f64(weight), 1e-6, cs[pc].numpy())
-    assert alt <= max(3, n * 512 // 500)
+    cap = max(3, n * 512 // 500)
+    print(f"[gpu] compress + finalize: {alt} admissible non-nearest values of {n * 512} "
+          f"checked (cap {cap})", flush=True)
+    assert alt <= cap

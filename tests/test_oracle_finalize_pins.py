@@ -2,7 +2,7 @@
 quantisation, GPT-J RoPE, the byte scatter into a packed KV page).
 
 Each check ties the oracle to something other than itself: hand-derived
-quantisation and slot fixtures, closed forms (a vector whose normalised values
+quantisation, slot and RoPE-row fixtures, closed forms (a vector whose normalised values
 are all +-1, quarter-turn rotations), torch's fp64 RMSNorm, rotation norms and
 a full closed-form output. The mutation tests at the end plant plausible
 mistakes in copies of the oracle functions and require a pin to fail.
@@ -22,7 +22,9 @@ def impl(**over):
     ns = SimpleNamespace(rms_norm=oc.rms_norm, quant_exponent=oc.quant_exponent,
                          quantize_nope=oc.quantize_nope, rope_gptj=oc.rope_gptj,
                          slot_byte_offsets=oc.slot_byte_offsets,
-                         finalize_output=oc.finalize_output)
+                         rope_position=oc.rope_position,
+                         finalize_output=oc.finalize_output,
+                         finalize_outputs=oc.finalize_outputs)
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -109,6 +111,11 @@ def pin_closed_form_output(f):
     assert np.array_equal(got, want)
 
 
+def pin_rope_rows(f):
+    for r in read_golden("rope_rows.txt"):
+        assert f.rope_position(int(r[0]), int(r[1])) == int(r[3]), r
+
+
 def pin_scatter(f):
     rng = np.random.default_rng(4)
     pages = 3
@@ -116,14 +123,15 @@ def pin_scatter(f):
     comp = rng.standard_normal((5, 512))
     cs = rng.standard_normal((300, 64))
     slots = [5, -1, 130, 3 * 64, 63]                      # padding and outside slots write nothing
-    pos = [127, 255, 200, 299, 150]                       # RoPE rows 0, 128, 128, 256, 128
-    out = oc.finalize_outputs(comp, np.ones(512), 1e-6, cs, pos, 128, slots, kv)
+    pos = [127, 255, 200, 299, 150]
+    rows = [0, 128, 128, 256, 128]                        # their RoPE rows at C = 128, by hand
+    out = f.finalize_outputs(comp, np.ones(512), 1e-6, cs, pos, 128, slots, kv)
     touched = np.zeros_like(kv, dtype=bool)
     for j, s in enumerate(slots):
         if s < 0 or s >= pages * 64:
             continue
         page, po, so = f.slot_byte_offsets(s)
-        payload, scale, _ = f.finalize_output(comp[j], np.ones(512), 1e-6, cs[(pos[j] // 128) * 128])
+        payload, scale, _ = f.finalize_output(comp[j], np.ones(512), 1e-6, cs[rows[j]])
         assert np.array_equal(out[page, po:po + 576], payload)
         assert np.array_equal(out[page, so:so + 8], scale)
         touched[page, po:po + 576] = True
@@ -132,7 +140,7 @@ def pin_scatter(f):
 
 
 ALL_PINS = [pin_quant_fixture, pin_slot_fixture, pin_rms_norm, pin_rope, pin_closed_form_output,
-            pin_scatter]
+            pin_rope_rows, pin_scatter]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS)
@@ -230,9 +238,16 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("kind", sorted(MUTANTS))
-def test_planted_mistake_is_caught(kind):
-    f = impl(**MUTANTS[kind])
+# Mistakes in the RoPE row are planted in the module itself, so that the
+# oracle's own finalize_outputs (which looks the row up per output) uses them.
+MODULE_MUTANTS = {
+    "rope_row_is_position": dict(rope_position=lambda p, c: int(p)),
+    "rope_row_is_chunk_index": dict(rope_position=lambda p, c: int(p) // int(c)),
+    "rope_row_is_chunk_end": dict(rope_position=lambda p, c: (int(p) // int(c) + 1) * int(c) - 1),
+}
+
+
+def _count_failing_pins(f):
     failed = 0
     for pin in ALL_PINS:
         try:
@@ -240,7 +255,21 @@ def test_planted_mistake_is_caught(kind):
                 pin(f)
         except (AssertionError, ValueError, IndexError, OverflowError):
             failed += 1
-    assert failed >= 1, kind
+    return failed
+
+
+@pytest.mark.parametrize("kind", sorted(MUTANTS))
+def test_planted_mistake_is_caught(kind):
+    assert _count_failing_pins(impl(**MUTANTS[kind])) >= 1, kind
+
+
+@pytest.mark.parametrize("kind", sorted(MODULE_MUTANTS))
+def test_planted_rope_row_mistake_is_caught(kind, monkeypatch):
+    for name, fn in MODULE_MUTANTS[kind].items():
+        monkeypatch.setattr(oc, name, fn)
+    failed = _count_failing_pins(impl())
+    # both the fixture pin and the scatter pin (through finalize_outputs) see it
+    assert failed >= 2, (kind, failed)
 
 
 def test_mutant_harness_is_faithful():
