@@ -191,17 +191,19 @@ PKV_API pkv_status pkv_combine(const pkv_decode_params* params, const float* o_p
 /* Test/debug: the element offset that the decode kernel's page walker computes
  * for every token of KV head kv_head, through the key-cache geometry
  * (k_page_stride). row_offsets int64 [S, max_seq_len]; entries at t >=
- * seq_lens[s] are set to -1. Uses the same partition / wave / block walk as
- * pkv_decode with the planned P. */
+ * seq_lens[s] are set to -1. Runs the split launch pkv_decode would run for
+ * these params (balanced or fixed partitions, the same page-list bounds and
+ * walker instantiation), recording each block's rows instead of reading them. */
 PKV_API pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
                              const int32_t* block_table, const int32_t* seq_lens,
                              int64_t* row_offsets, void* stream);
 
 /* Test/debug: copy every valid token row of `cache` (key-cache geometry,
- * k_page_stride) into dense bf16 [S, max_seq_len, Hkv, D] through the decode
- * kernel's page walker and tile loaders (K-operand and V-operand lane
- * layouts both exercised: which = 0 uses the K loader, 1 the V loader).
- * Rows at t >= seq_lens[s] are left untouched. */
+ * k_page_stride) into dense bf16 [S, max_seq_len, Hkv, D] through the split
+ * walk pkv_decode would run for these params and its block loaders: which = 0
+ * uses the K loader of that plan (the MFMA operand layout for one sequence,
+ * whole rows for a batch), 1 the V loader (whole rows). Rows at t >=
+ * seq_lens[s] are left untouched. */
 PKV_API pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which,
                             const void* cache, const int32_t* block_table,
                             const int32_t* seq_lens, void* dense, void* stream);

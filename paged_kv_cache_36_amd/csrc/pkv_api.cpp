@@ -46,6 +46,7 @@ struct Plan {
   int32_t n_parts = 0;      // fixed partitions: ceil(max_seq_len / P)
   int32_t grid = 0;         // balanced: workgroups G
   bool refetch = false;     // a segment may span more than the walker's 64 page ids
+  bool k_rows = false;      // K loaded as whole rows and staged through LDS
   size_t o_part_bytes = 0;
   size_t lse_bytes = 0;
   size_t workspace = 0;
@@ -73,6 +74,12 @@ pkv_status check_params(const pkv_decode_params* p) {
   return PKV_OK;
 }
 
+// K load layout. Whole rows (full 128-byte lines, staged through LDS for the
+// MFMA operand) stream faster than the operand layout's half-line reads, at
+// the cost of one more LDS round trip per block; a batch has enough blocks in
+// flight to hide it, a single sequence's short decode does not.
+bool k_rows_for(const pkv_decode_params* p) { return p->num_seqs > 1; }
+
 // Fixed partitions (pkv_split, pkv_decode_partials, and pkv_decode with an
 // explicit partition size).
 Plan make_fixed_plan(const pkv_decode_params* p) {
@@ -92,6 +99,7 @@ Plan make_fixed_plan(const pkv_decode_params* p) {
   pl.P = P;
   pl.n_parts = p->max_seq_len > 0 ? (p->max_seq_len + P - 1) / P : 1;
   pl.refetch = pkv::partition_needs_refetch(P, p->block_size);
+  pl.k_rows = k_rows_for(p);
   if (pl.n_parts > 1) {
     const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * pl.n_parts;
     pl.o_part_bytes = round_up(rows * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
@@ -127,6 +135,7 @@ Plan make_decode_plan(const pkv_decode_params* p) {
       p->max_seq_len, ((t_max + g - 1) / g + 1) * pkv::kTileTokens);
   pl.refetch = pkv::partition_needs_refetch(static_cast<int32_t>((seg_tokens + 63) / 64 * 64),
                                             p->block_size);
+  pl.k_rows = k_rows_for(p);
   const size_t slots = static_cast<size_t>(g) + static_cast<size_t>(p->num_seqs) * p->num_kv_heads;
   pl.o_part_bytes = round_up(slots * pkv::kGroup * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
   pl.lse_bytes = round_up(slots * pkv::kGroup * sizeof(float), kWorkspaceAlign);
@@ -178,6 +187,14 @@ pkv_status check_inputs(const void* q, const void* k, const void* v, const int32
 }
 
 pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+pkv::SplitChoice split_choice(const Plan& pl) {
+  pkv::SplitChoice c;
+  c.balanced = pl.balanced;
+  c.refetch = pl.refetch;
+  c.k_rows = pl.k_rows;
+  return c;
+}
 
 pkv_status check_workspace(const Plan& pl, const void* workspace, size_t workspace_bytes) {
   if (pl.workspace > 0 &&
@@ -250,6 +267,49 @@ size_t prefill_workspace(const pkv_prefill_params* p, int32_t splits) {
 
 }  // namespace
 
+namespace pkv {
+
+size_t decode_workspace(const pkv_decode_params* params) {
+  if (check_params(params) != PKV_OK) return 0;
+  return make_decode_plan(params).workspace;
+}
+
+pkv_status decode_call(const pkv_decode_params* params, const void* q, const void* key_cache,
+                       const void* value_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, void* out, float* out_f32, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  pkv_status st = check_params(params);
+  if (st != PKV_OK) return st;
+  if (params->num_seqs == 0) return PKV_OK;
+  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
+  if (st != PKV_OK) return st;
+  if (!out || !aligned(out, 16) || (out_f32 != nullptr && !aligned(out_f32, 16)))
+    return PKV_ERR_NULL;
+  const Plan pl = make_decode_plan(params);
+  st = check_workspace(pl, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  log_plan("decode", params, pl);
+
+  pkv::LaunchArgs a = base_args(params, pl);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(key_cache);
+  a.v = static_cast<const uint16_t*>(value_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.out_f32 = out_f32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!pl.balanced && pl.n_parts == 1)
+    return hip_status(pkv::launch_split(a, /*direct=*/true, pl.k_rows, s));
+  carve_workspace(pl, workspace, a);
+  st = pl.balanced ? hip_status(pkv::launch_balanced_split(a, pl.refetch, pl.k_rows, s))
+                   : hip_status(pkv::launch_split(a, /*direct=*/false, pl.k_rows, s));
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_combine(a, pl.balanced, s));
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
@@ -289,41 +349,15 @@ pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info) {
 }
 
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* params) {
-  if (check_params(params) != PKV_OK) return 0;
-  return make_decode_plan(params).workspace;
+  return pkv::decode_workspace(params);
 }
 
 pkv_status pkv_decode(const pkv_decode_params* params, const void* q, const void* key_cache,
                       const void* value_cache, const int32_t* block_table,
                       const int32_t* seq_lens, void* out, float* out_f32, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  pkv_status st = check_params(params);
-  if (st != PKV_OK) return st;
-  if (params->num_seqs == 0) return PKV_OK;
-  st = check_inputs(q, key_cache, value_cache, block_table, seq_lens);
-  if (st != PKV_OK) return st;
-  if (!out || !aligned(out, 16) || (out_f32 != nullptr && !aligned(out_f32, 16)))
-    return PKV_ERR_NULL;
-  const Plan pl = make_decode_plan(params);
-  st = check_workspace(pl, workspace, workspace_bytes);
-  if (st != PKV_OK) return st;
-  log_plan("decode", params, pl);
-
-  pkv::LaunchArgs a = base_args(params, pl);
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(key_cache);
-  a.v = static_cast<const uint16_t*>(value_cache);
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = static_cast<uint16_t*>(out);
-  a.out_f32 = out_f32;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!pl.balanced && pl.n_parts == 1) return hip_status(pkv::launch_split(a, /*direct=*/true, s));
-  carve_workspace(pl, workspace, a);
-  st = pl.balanced ? hip_status(pkv::launch_balanced_split(a, pl.refetch, s))
-                   : hip_status(pkv::launch_split(a, /*direct=*/false, s));
-  if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_combine(a, pl.balanced, s));
+  return pkv::decode_call(params, q, key_cache, value_cache, block_table, seq_lens, out, out_f32,
+                          workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_split_balanced(const pkv_decode_params* params, const void* q,
@@ -346,7 +380,8 @@ pkv_status pkv_split_balanced(const pkv_decode_params* params, const void* q,
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   carve_workspace(pl, workspace, a);
-  return hip_status(pkv::launch_balanced_split(a, pl.refetch, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      pkv::launch_balanced_split(a, pl.refetch, pl.k_rows, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_combine_balanced(const pkv_decode_params* params, const int32_t* seq_lens,
@@ -395,7 +430,7 @@ pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
   a.out = static_cast<uint16_t*>(out);
   a.out_f32 = out_f32;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(pkv::launch_split(a, /*direct=*/false, s));
+  st = hip_status(pkv::launch_split(a, /*direct=*/false, pl.k_rows, s));
   if (st != PKV_OK) return st;
   return hip_status(pkv::launch_combine(a, /*balanced=*/false, s));
 }
@@ -421,7 +456,8 @@ pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void*
   a.seq_lens = seq_lens;
   a.o_part = o_partial;
   a.lse_part = lse_partial;
-  return hip_status(pkv::launch_split(a, /*direct=*/false, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      pkv::launch_split(a, /*direct=*/false, pl.k_rows, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,
@@ -451,12 +487,14 @@ pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,
   if (kv_head < 0 || kv_head >= params->num_kv_heads) return PKV_ERR_SHAPE;
   if (params->num_seqs == 0) return PKV_OK;
   if (!block_table || !seq_lens || !row_offsets || !aligned(row_offsets, 8)) return PKV_ERR_NULL;
-  const Plan pl = make_fixed_plan(params);
+  const Plan pl = make_decode_plan(params);
   pkv::LaunchArgs a = base_args(params, pl);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
+  a.dbg_offsets = row_offsets;
+  a.dbg_kv_head = kv_head;
   return hip_status(
-      pkv::launch_debug_resolve(a, kv_head, row_offsets, static_cast<hipStream_t>(stream)));
+      pkv::launch_debug_resolve(a, split_choice(pl), static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which, const void* cache,
@@ -468,13 +506,15 @@ pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which, cons
   if (params->num_seqs == 0) return PKV_OK;
   if (!cache || !block_table || !seq_lens || !dense || !aligned(cache, 16) || !aligned(dense, 16))
     return PKV_ERR_NULL;
-  const Plan pl = make_fixed_plan(params);
+  const Plan pl = make_decode_plan(params);
   pkv::LaunchArgs a = base_args(params, pl);
   a.k = static_cast<const uint16_t*>(cache);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  return hip_status(pkv::launch_debug_gather(a, which, static_cast<uint16_t*>(dense),
-                                             static_cast<hipStream_t>(stream)));
+  a.dbg_dense = static_cast<uint16_t*>(dense);
+  a.dbg_which = which;
+  return hip_status(
+      pkv::launch_debug_gather(a, split_choice(pl), static_cast<hipStream_t>(stream)));
 }
 
 int32_t pkv_probe_sink_floats(void) { return pkv::probe_sink_floats(); }

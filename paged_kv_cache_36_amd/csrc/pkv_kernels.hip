@@ -111,13 +111,14 @@ struct PageWalker {
 // Loads through it carry a VGPR offset per lane and an SGPR offset per row, so
 // one block costs one base pointer instead of a 64-bit address per row.
 constexpr int kBufferWord3 = 0x00020000;   // raw 32-bit data format (gfx9 family)
-// Cache policy of the block loads. A V instruction reads whole 512-byte rows
-// (full 128-byte lines) and every V byte is read once, so V streams past the
-// caches (nontemporal). A K instruction reads 64 of the 128 bytes of each of
-// 16 lines (the MFMA operand layout) and the next instruction reads the other
-// half, so K keeps the default policy and the second half hits in L2.
-constexpr int kPolicyK = 0;
-constexpr int kPolicyV = 2;                // nontemporal
+// Cache policies of the block loads. A row-layout instruction reads whole
+// 512-byte rows (full 128-byte lines) and every byte is read once, so such
+// loads stream past the caches (nontemporal). An operand-layout K instruction
+// reads 64 of the 128 bytes of each of 16 lines (the MFMA A-operand layout)
+// and the next instruction reads the other half, so it keeps the default
+// policy and the second half hits in L2.
+constexpr int kPolicyOperand = 0;
+constexpr int kPolicyRows = 2;             // nontemporal
 // With live == false the resource has no records: every load through it
 // returns 0 without touching memory (used for the prefetch past a wave's last
 // block, so the loop issues the same loads on every path).
@@ -127,51 +128,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* row
                                            live ? kWaveTokens * row_bytes : 0, kBufferWord3);
 }
 
-// K block in the A-operand layout of v_mfma_f32_16x16x32_bf16: lane l holds
-// token (l & 15), and for k-step ks the 8 dims 32 ks + 8 (l >> 4) .. + 7.
+// A block of 16 rows of one KV head in registers, 8 x 16 bytes per lane, in
+// one of two layouts (below).
+struct RowRegs {
+  u32x4 r[8];
+};
+
+// Operand layout (K only): the A operand of v_mfma_f32_16x16x32_bf16. Lane l
+// holds token (l & 15), and for k-step ks the 8 dims 32 ks + 8 (l >> 4) .. + 7.
 // All 16 rows are read even past the last valid token: a block never leaves
 // its page, so they are in-bounds page memory, and their scores are masked to
 // -inf before use. `voff` is the lane's byte offset, k_lane_offset().
-struct KBlock {
-  u32x4 r[8];
-};
 __device__ __forceinline__ int k_lane_offset(int lane, int32_t row_bytes) {
   return (lane & 15) * row_bytes + 16 * (lane >> 4);
 }
-__device__ __forceinline__ void load_k_block(const uint16_t* rows, int32_t row_bytes, int voff,
-                                             KBlock& kb, bool live = true) {
+__device__ __forceinline__ void load_k_operand(const uint16_t* rows, int32_t row_bytes, int voff,
+                                               RowRegs& kb, bool live = true) {
   const __amdgpu_buffer_rsrc_t rs = block_rsrc(rows, row_bytes, live);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
-    kb.r[ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * ks, 0, kPolicyK);
+    kb.r[ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 64 * ks, 0, kPolicyOperand);
 }
 
-// V block: two 512-byte rows per wave instruction (16 bytes per lane, the
-// widest load, so the block costs 8 instructions): r[i] of lane l holds dims
-// 8 (l & 31) .. + 7 of row v_row(i, l) = 2 i + (l >> 5). Rows after `last`
-// (the block's last valid row, 0..15) repeat row `last`: finite data whose
-// softmax weights are exactly 0 (V rows past the sequence may be NaN, and
-// 0 * NaN is NaN).
-struct VBlock {
-  u32x4 r[8];
-};
-__device__ __forceinline__ int v_row(int i, int lane) { return 2 * i + (lane >> 5); }
-__device__ __forceinline__ void load_v_block(const uint16_t* rows, int32_t row_bytes, int last,
-                                             int lane, VBlock& vb, bool live = true) {
+// Row layout (V, and K when it is staged through LDS): two 512-byte rows per
+// wave instruction (16 bytes per lane, the widest load, so the block costs 8
+// instructions): r[i] of lane l holds dims 8 (l & 31) .. + 7 of row
+// block_row(i, l) = 2 i + (l >> 5). Rows after `last` (the block's last valid
+// row, 0..15) repeat row `last`: finite data whose softmax weights are exactly
+// 0 (rows past the sequence may be NaN, and 0 * NaN is NaN).
+__device__ __forceinline__ int block_row(int i, int lane) { return 2 * i + (lane >> 5); }
+__device__ __forceinline__ void load_rows(const uint16_t* rows, int32_t row_bytes, int last,
+                                          int lane, RowRegs& rb, bool live = true) {
   const __amdgpu_buffer_rsrc_t rs = block_rsrc(rows, row_bytes, live);
 #pragma unroll
   for (int i = 0; i < kWaveTokens / 2; ++i) {
-    const int rr = min(v_row(i, lane), last);
-    vb.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, rr * row_bytes + 16 * (lane & 31), 0,
-                                                    kPolicyV);
+    const int rr = min(block_row(i, lane), last);
+    rb.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, rr * row_bytes + 16 * (lane & 31), 0,
+                                                    kPolicyRows);
   }
 }
 
 // LDS geometry (elements of 16 bits). Rows are padded so that the transposed
-// V reads (16 rows x 32 bytes per instruction) and the q fragment reads fall
-// on distinct banks.
+// V reads (16 rows x 32 bytes per instruction), the K operand reads (16 rows
+// x 16 bytes) and the q fragment reads fall on distinct banks.
 constexpr int kQStride = kD + 8;          // q row: 256 dims + 16 bytes pad
+constexpr int kKStride = kD + 8;          // K row: 256 dims + 16 bytes pad
 constexpr int kVStride = kD + 16;         // V row: 256 dims + 32 bytes pad
+constexpr int kKWaveElems = kWaveTokens * kKStride;
 constexpr int kVWaveElems = kWaveTokens * kVStride;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -194,8 +197,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 // One 16-token block of one wave:
-//  scores S^T[token][head] = K . q by 8 MFMAs (16x16x32, K from registers,
-//  q fragments from LDS), online softmax update, then P.V on MFMA:
+//  scores S^T[token][head] = K . q by 8 MFMAs (16x16x32, q fragments from
+//  LDS; K from registers in the operand layout, or, with kKRows, from its
+//  rows staged in LDS), online softmax update, then P.V on MFMA:
 //  O^T[dim][head] += V^T[dim][token] . P^T[token][head] with 16x16x16 MFMAs.
 //  The P^T operand is the score tile's own layout (lane: head n, tokens
 //  4j..4j+3); it is split p = p_hi + p_lo into two bf16 operands so the
@@ -204,26 +208,33 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //  k-th value is element i % 4 of the 8 bytes addressed by lane i / 4 + 4 k,
 //  so lane (j, s) addresses V[4 j + s / 4][16 db + 4 (s % 4)] and receives
 //  V[4 j + k][16 db + i].
-__device__ __forceinline__ void process_block(const KBlock& kb, const VBlock& vb,
-                                              const uint16_t* lds_q, uint16_t* lds_vw, int t,
-                                              int t_end, float scale_log2, int lane,
-                                              WaveState& st) {
+template <bool kKRows>
+__device__ __forceinline__ void process_block(const RowRegs& kb, const RowRegs& vb,
+                                              const uint16_t* lds_q, uint16_t* lds_kw,
+                                              uint16_t* lds_vw, int t, int t_end,
+                                              float scale_log2, int lane, WaveState& st) {
   const int n = lane & 15;   // head column of the score tile
   const int j = lane >> 4;   // row group of the score tile (tokens 4j .. 4j+3)
 
-  // stage this block's V rows (lane holds dims 4 lane .. +3 of each token)
-  // into LDS for the transposing reads below
+  // stage this block's V rows (and K rows) into LDS for the reads below
 #pragma unroll
-  for (int i = 0; i < kWaveTokens / 2; ++i)
-    *reinterpret_cast<u32x4*>(lds_vw + v_row(i, lane) * kVStride + 8 * (lane & 31)) = vb.r[i];
+  for (int i = 0; i < kWaveTokens / 2; ++i) {
+    *reinterpret_cast<u32x4*>(lds_vw + block_row(i, lane) * kVStride + 8 * (lane & 31)) = vb.r[i];
+    if (kKRows)
+      *reinterpret_cast<u32x4*>(lds_kw + block_row(i, lane) * kKStride + 8 * (lane & 31)) =
+          kb.r[i];
+  }
+  if (kKRows) wave_lds_sync();   // K (and V) rows visible to the whole wave
 
   // scores
   const uint16_t* qrow = lds_q + min(n, kG - 1) * kQStride + 8 * j;
+  const uint16_t* krow = lds_kw + n * kKStride + 8 * j;   // operand of token n, dims 8 j ..
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.r[ks]),
+    const u32x4 kv = kKRows ? *reinterpret_cast<const u32x4*>(krow + 32 * ks) : kb.r[ks];
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv),
                                                 __builtin_bit_cast(bf16x8, qv), sc, 0, 0, 0);
   }
 
@@ -265,7 +276,7 @@ __device__ __forceinline__ void process_block(const KBlock& kb, const VBlock& vb
   const s16x4 p_hi = __builtin_bit_cast(s16x4, u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)});
   const s16x4 p_lo = __builtin_bit_cast(s16x4, u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)});
 
-  wave_lds_sync();   // V rows visible to the whole wave
+  if (!kKRows) wave_lds_sync();   // V rows visible to the whole wave
   const int s = lane & 15;
   const uint16_t* vsrc = lds_vw + (4 * j + (s >> 2)) * kVStride + 4 * (s & 3);
   s16x4 va[16];
@@ -279,26 +290,30 @@ __device__ __forceinline__ void process_block(const KBlock& kb, const VBlock& vb
 #pragma unroll
   for (int db = 0; db < 16; ++db)
     st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[db], p_lo, st.acc[db], 0, 0, 0);
-  wave_lds_sync();   // V rows consumed before the next block overwrites them
+  wave_lds_sync();   // rows consumed before the next block overwrites them
 }
 
 // Block loads of one wave: K and V of tokens [tt, tt + 16) for the walker's
 // current block. Past t_end the loads go through an empty resource (no
 // memory traffic), so every path of the loop issues the same loads and each
 // block waits only for its own data.
+template <bool kKRows>
 struct BlockLoader {
   const LaunchArgs& a;
   const PageWalker& walker;
   int t_end, row_stride, row_bytes, head_off, voff_k, lane;
-  __device__ __forceinline__ void operator()(int tt, KBlock& kk, VBlock& vv) const {
+  __device__ __forceinline__ void operator()(int tt, RowRegs& kk, RowRegs& vv) const {
     const bool live = tt < t_end;
     // last valid row of the block (select + min only: stays on the scalar unit)
     const int n_left = live ? t_end - tt : kWaveTokens;
     const int last = (n_left < kWaveTokens ? n_left : kWaveTokens) - 1;
-    load_k_block(a.k + walker.base(a.k_page_stride, row_stride, head_off), row_bytes, voff_k, kk,
-                 live);
-    load_v_block(a.v + walker.base(a.v_page_stride, row_stride, head_off), row_bytes, last, lane,
-                 vv, live);
+    const uint16_t* krows = a.k + walker.base(a.k_page_stride, row_stride, head_off);
+    if (kKRows)
+      load_rows(krows, row_bytes, last, lane, kk, live);
+    else
+      load_k_operand(krows, row_bytes, voff_k, kk, live);
+    load_rows(a.v + walker.base(a.v_page_stride, row_stride, head_off), row_bytes, last, lane, vv,
+              live);
   }
 };
 
@@ -308,22 +323,23 @@ struct BlockLoader {
 // (ka, va). kRefetch selects the walker that may refetch the page list inside
 // the loop (a refetch makes the wave wait for all of its loads, so the common
 // case keeps it out of the loop entirely).
-template <bool kRefetch>
+template <bool kKRows, bool kRefetch>
 __device__ __forceinline__ void stream_partition(const LaunchArgs& a, PageWalker& walker,
-                                                 const BlockLoader& load, KBlock& ka, VBlock& va,
-                                                 const uint16_t* lds_q, uint16_t* lds_vw, int t,
+                                                 const BlockLoader<kKRows>& load, RowRegs& ka,
+                                                 RowRegs& va, const uint16_t* lds_q,
+                                                 uint16_t* lds_kw, uint16_t* lds_vw, int t,
                                                  int t_end, int lane, WaveState& st) {
-  KBlock kb;
-  VBlock vb;
+  RowRegs kb;
+  RowRegs vb;
   for (;;) {
     walker.advance<kRefetch>(kTileTokens, lane);
     load(t + kTileTokens, kb, vb);
-    process_block(ka, va, lds_q, lds_vw, t, t_end, a.scale_log2, lane, st);
+    process_block<kKRows>(ka, va, lds_q, lds_kw, lds_vw, t, t_end, a.scale_log2, lane, st);
     t += kTileTokens;
     if (t >= t_end) break;
     walker.advance<kRefetch>(kTileTokens, lane);
     load(t + kTileTokens, ka, va);
-    process_block(kb, vb, lds_q, lds_vw, t, t_end, a.scale_log2, lane, st);
+    process_block<kKRows>(kb, vb, lds_q, lds_kw, lds_vw, t, t_end, a.scale_log2, lane, st);
     t += kTileTokens;
     if (t >= t_end) break;
   }
@@ -344,11 +360,14 @@ __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
 }
 
 // LDS of one split workgroup.
+template <bool kKRows>
 struct SplitLds {
   uint16_t q[kG * kQStride];
   // per-wave V staging rows; after the loop each wave reuses its own slice
   // for its partial output [kG][kD] fp32
   uint16_t v[kWaves][kVWaveElems];
+  // per-wave K staging rows (only with kKRows)
+  uint16_t k[kKRows ? kWaves : 1][kKRows ? kKWaveElems : 8];
   alignas(16) float m[kWaves][8];
   alignas(16) float l[kWaves][8];
 };
@@ -365,10 +384,6 @@ enum SegmentTarget : int {
   kToSlot = 2,         // o_part[slot, h % 6, :], lse_part[slot, h % 6] (balanced split)
 };
 
-// One workgroup's pass over tokens [t_begin, t_end) of sequence s for KV
-// head g: the 4 waves stream their blocks, their states are merged through
-// LDS and the merged (o, lse) of the 6 query heads is written to `target`.
-// Ends with a workgroup barrier so the LDS can be reused right away.
 // The loads a segment starts with: the wave's page list and its 16 bytes of q.
 // They depend on the segment's first token and a bound on its pages only, so
 // the fixed-partition kernel issues them before its sequence length arrives.
@@ -376,23 +391,22 @@ struct SegmentStart {
   PageWalker walker;
   u32x4 qv;
 };
-__device__ __forceinline__ SegmentStart begin_segment(const LaunchArgs& a, int s, int g,
-                                                      int t_begin, int32_t page_end) {
-  SegmentStart su;
-  su.walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size,
-                 t_begin + wave_id() * kWaveTokens, page_end, lane_id());
-  // q: 6 rows x 512 bytes, 16 bytes per thread for threads < 192 (the others
-  // load a duplicate and do not store it)
-  const int64_t head0 = static_cast<int64_t>(s) * a.num_kv_heads * kG + g * kG;
-  const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
-  su.qv = *reinterpret_cast<const u32x4*>(a.q + (head0 + qh) * kD + 8 * qc);
-  return su;
+// The walker of a segment that starts at token t_begin: wave w begins at
+// t_begin + 16 w, with the page ids of logical pages up to page_end listed.
+__device__ __forceinline__ void segment_walker(const LaunchArgs& a, int s, int t_begin,
+                                               int32_t page_end, PageWalker& walker) {
+  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size,
+              t_begin + wave_id() * kWaveTokens, page_end, lane_id());
 }
 
-template <bool kRefetch>
-__device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, SegmentStart& su,
-                                            int s, int g, int t_begin, int t_end,
-                                            SegmentTarget target, int64_t index) {
+// One workgroup's pass over tokens [t_begin, t_end) of sequence s for KV
+// head g: the 4 waves stream their blocks, their states are merged through
+// LDS and the merged (o, lse) of the 6 query heads is written to `target`.
+// Ends with a workgroup barrier so the LDS can be reused right away.
+template <bool kKRows, bool kRefetch>
+__device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows>& lds,
+                                            SegmentStart& su, int s, int g, int t_begin,
+                                            int t_end, SegmentTarget target, int64_t index) {
   const int lane = lane_id();
   const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
@@ -401,11 +415,12 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   const int head_off = g * kD;
 
   // Start-up, ordered so the first K/V loads wait on one memory round trip:
-  // the page list and q were fetched together (begin_segment), the first
+  // the page list and q were fetched together (DecodeOp::begin), the first
   // block is issued as soon as the page list is in, and q goes to LDS while
   // that block is in flight. Every wave issues the same loads (a wave with no
   // block loads through an empty resource), so the waits stay exact.
   uint16_t* lds_vw = lds.v[w];
+  uint16_t* lds_kw = lds.k[kKRows ? w : 0];
   int t = t_begin + w * kWaveTokens;
   const bool active = t < t_end;
   PageWalker& walker = su.walker;
@@ -413,10 +428,10 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
   const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
   __builtin_amdgcn_sched_barrier(0);   // keep the q load ahead of the block loads
   const int row_bytes = row_stride * 2;
-  const BlockLoader load{a, walker, t_end, row_stride, row_bytes, head_off,
-                         k_lane_offset(lane, row_bytes), lane};
-  KBlock ka;
-  VBlock va;
+  const BlockLoader<kKRows> load{a,         walker,   t_end, row_stride,
+                                 row_bytes, head_off, k_lane_offset(lane, row_bytes), lane};
+  RowRegs ka;
+  RowRegs va;
   load(t, ka, va);
   __builtin_amdgcn_sched_barrier(0);   // issue the first block before waiting for q
   if (q_thread) *reinterpret_cast<u32x4*>(lds.q + qh * kQStride + 8 * qc) = su.qv;
@@ -428,7 +443,8 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds& lds, 
 #pragma unroll
   for (int db = 0; db < 16; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (active)
-    stream_partition<kRefetch>(a, walker, load, ka, va, lds.q, lds_vw, t, t_end, lane, st);
+    stream_partition<kKRows, kRefetch>(a, walker, load, ka, va, lds.q, lds_kw, lds_vw, t, t_end,
+                                       lane, st);
 
   // merge the four waves' states
   const int n = lane & 15;
@@ -511,29 +527,155 @@ __device__ __forceinline__ void zero_rows(const LaunchArgs& a, int s, int g) {
 }
 
 // ---------------------------------------------------------------------------
+// What a split workgroup does with each of its segments. The split kernels
+// below decide which segments a workgroup takes (fixed partitions or the
+// balanced share) and hand each one to an Op:
+//  - DecodeOp runs the attention pass (run_segment);
+//  - DebugResolveOp and DebugGatherOp walk the same segment with the same
+//    walker instantiation and record what the decode pass would read (the
+//    row offsets, or the rows through the decode's own loaders), so the
+//    bit-exact address tests cover the code the decode kernels run.
+// ---------------------------------------------------------------------------
+template <bool kKRows>
+struct DecodeOp {
+  using Lds = SplitLds<kKRows>;
+  static __device__ __forceinline__ SegmentStart begin(const LaunchArgs& a, int s, int g,
+                                                       int t_begin, int32_t page_end) {
+    SegmentStart su;
+    segment_walker(a, s, t_begin, page_end, su.walker);
+    // q: 6 rows x 512 bytes, 16 bytes per thread for threads < 192 (the
+    // others load a duplicate and do not store it)
+    const int64_t head0 = static_cast<int64_t>(s) * a.num_kv_heads * kG + g * kG;
+    const int qh = min(static_cast<int>(threadIdx.x >> 5), kG - 1), qc = threadIdx.x & 31;
+    su.qv = *reinterpret_cast<const u32x4*>(a.q + (head0 + qh) * kD + 8 * qc);
+    return su;
+  }
+  template <bool kRefetch>
+  static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds& lds, SegmentStart& su,
+                                                 int s, int g, int t_begin, int t_end,
+                                                 SegmentTarget target, int64_t index) {
+    run_segment<kKRows, kRefetch>(a, lds, su, s, g, t_begin, t_end, target, index);
+  }
+  static __device__ __forceinline__ void empty(const LaunchArgs& a, int s, int g) {
+    zero_rows(a, s, g);
+  }
+};
+
+struct NoLds {
+  int unused;
+};
+
+// The blocks of one wave in a segment, in the order stream_partition visits
+// them: block t at the walker state reached after (t - first) / 64 advances.
+template <bool kRefetch, class F>
+__device__ __forceinline__ void walk_blocks(PageWalker& walker, int t_begin, int t_end, F&& f) {
+  int t = t_begin + wave_id() * kWaveTokens;
+  if (t >= t_end) return;
+  for (;;) {
+    f(t, walker);
+    t += kTileTokens;
+    if (t >= t_end) break;
+    walker.advance<kRefetch>(kTileTokens, lane_id());
+  }
+}
+
+struct DebugResolveOp {
+  using Lds = NoLds;
+  static __device__ __forceinline__ SegmentStart begin(const LaunchArgs& a, int s, int,
+                                                       int t_begin, int32_t page_end) {
+    SegmentStart su;
+    segment_walker(a, s, t_begin, page_end, su.walker);
+    return su;
+  }
+  template <bool kRefetch>
+  static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds&, SegmentStart& su,
+                                                 int s, int g, int t_begin, int t_end,
+                                                 SegmentTarget, int64_t) {
+    if (g != a.dbg_kv_head) return;
+    const int lane = lane_id();
+    const int row_stride = a.num_kv_heads * kD;
+    walk_blocks<kRefetch>(su.walker, t_begin, t_end, [&](int t, const PageWalker& wk) {
+      const int nv = min(kWaveTokens, t_end - t);
+      const int64_t base = wk.base(a.k_page_stride, row_stride, g * kD);
+      if (lane < nv)
+        a.dbg_offsets[static_cast<int64_t>(s) * a.max_seq_len + t + lane] =
+            base + static_cast<int64_t>(lane) * row_stride;
+    });
+  }
+  static __device__ __forceinline__ void empty(const LaunchArgs&, int, int) {}
+};
+
+// which == 0: the K loader of this instantiation (operand layout, or rows
+// with kKRows); which == 1: the row loader V uses. Reads a.k (the cache under
+// test) with the key-cache page stride.
+template <bool kKRows>
+struct DebugGatherOp {
+  using Lds = NoLds;
+  static __device__ __forceinline__ SegmentStart begin(const LaunchArgs& a, int s, int,
+                                                       int t_begin, int32_t page_end) {
+    SegmentStart su;
+    segment_walker(a, s, t_begin, page_end, su.walker);
+    return su;
+  }
+  template <bool kRefetch>
+  static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds&, SegmentStart& su,
+                                                 int s, int g, int t_begin, int t_end,
+                                                 SegmentTarget, int64_t) {
+    const int lane = lane_id();
+    const int row_stride = a.num_kv_heads * kD;
+    const int row_bytes = row_stride * 2;
+    walk_blocks<kRefetch>(su.walker, t_begin, t_end, [&](int t, const PageWalker& wk) {
+      const int nv = min(kWaveTokens, t_end - t);
+      const uint16_t* rows = a.k + wk.base(a.k_page_stride, row_stride, g * kD);
+      uint16_t* dense = a.dbg_dense +
+                        ((static_cast<int64_t>(s) * a.max_seq_len + t) * a.num_kv_heads + g) * kD;
+      const int64_t dense_row = static_cast<int64_t>(a.num_kv_heads) * kD;
+      RowRegs rb;
+      if (a.dbg_which == 0 && !kKRows) {
+        load_k_operand(rows, row_bytes, k_lane_offset(lane, row_bytes), rb);
+        const int i = lane & 15;
+        if (i < nv) {
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            *reinterpret_cast<u32x4*>(dense + i * dense_row + 32 * ks + 8 * (lane >> 4)) = rb.r[ks];
+        }
+      } else {
+        load_rows(rows, row_bytes, nv - 1, lane, rb);
+#pragma unroll
+        for (int i = 0; i < kWaveTokens / 2; ++i) {
+          const int rr = block_row(i, lane);
+          if (rr < nv) *reinterpret_cast<u32x4*>(dense + rr * dense_row + 8 * (lane & 31)) = rb.r[i];
+        }
+      }
+    });
+  }
+  static __device__ __forceinline__ void empty(const LaunchArgs&, int, int) {}
+};
+
+// ---------------------------------------------------------------------------
 // Split-KV partition kernel, fixed partitions of P tokens: one workgroup per
 // (sequence, partition, KV head).
 // kRefetch: the partition may span more than 64 pages (pages smaller than
 // P / 63 tokens), so the page list is refetched inside the loop; chosen on
 // the host from P and the block size.
 // ---------------------------------------------------------------------------
-template <bool kDirect, bool kRefetch>
+template <class Op, bool kDirect, bool kRefetch>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
-  __shared__ __attribute__((aligned(16))) SplitLds lds;
+  __shared__ __attribute__((aligned(16))) typename Op::Lds lds;
   const SplitCoord c = split_coord(a);
   const int t_begin = c.part * a.partition_tokens;
   // the partition's pages as far as max_seq_len reaches (host-checked to fit
   // the table row), so the page list needs no sequence length
   const int t_cap = min(t_begin + a.partition_tokens, a.max_seq_len);
-  SegmentStart su = begin_segment(a, c.s, c.g, t_begin, PageWalker::pages_for(t_cap, a.block_size));
+  SegmentStart su = Op::begin(a, c.s, c.g, t_begin, PageWalker::pages_for(t_cap, a.block_size));
   const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
   if (t_begin >= seq_len) {
-    if (kDirect && c.part == 0) zero_rows(a, c.s, c.g);   // empty sequence
+    if (kDirect && c.part == 0) Op::empty(a, c.s, c.g);   // empty sequence
     return;
   }
   const int t_end = min(t_cap, seq_len);
-  run_segment<kRefetch>(a, lds, su, c.s, c.g, t_begin, t_end,
-                        kDirect ? kToOutput : kToPartition, c.part);
+  Op::template segment<kRefetch>(a, lds, su, c.s, c.g, t_begin, t_end,
+                                 kDirect ? kToOutput : kToPartition, c.part);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,15 +688,15 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
 // slot w + (s * Hkv + g): along the range boundaries the pair (w, s*Hkv + g)
 // moves monotonically, so these slots are distinct. Tile prefix sums are
 // computed by every workgroup from seq_lens; workgroup 0 also stores them for
-// the combine kernel.
+// the combine kernel (when a.prefix is set).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tiles_of(int seq_len) {
   return (seq_len + kTileTokens - 1) / kTileTokens;
 }
 
-template <bool kRefetch>
+template <class Op, bool kRefetch>
 __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs a) {
-  __shared__ __attribute__((aligned(16))) SplitLds lds;
+  __shared__ __attribute__((aligned(16))) typename Op::Lds lds;
   __shared__ int32_t pref[kMaxBalancedSeqs + 1];   // units before sequence s (x Hkv)
   const int S = a.num_seqs;
   const int hkv = a.num_kv_heads;
@@ -577,7 +719,7 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
     }
   }
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0 && a.prefix != nullptr)
     for (int i = threadIdx.x; i <= S; i += kThreads) a.prefix[i] = pref[i];
 
   // G_eff = min(G, T) workgroups take part, so every range is non-empty and
@@ -607,9 +749,9 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
     const int64_t seg_end = min(u1, base + static_cast<int64_t>(g + 1) * n);
     const int t_begin = tile * kTileTokens;
     const int t_end = min(static_cast<int>(tile + (seg_end - u)) * kTileTokens, seq_len);
-    SegmentStart su = begin_segment(a, s, g, t_begin, PageWalker::pages_for(t_end, a.block_size));
-    run_segment<kRefetch>(a, lds, su, s, g, t_begin, t_end, kToSlot,
-                          wg + static_cast<int64_t>(s) * hkv + g);
+    SegmentStart su = Op::begin(a, s, g, t_begin, PageWalker::pages_for(t_end, a.block_size));
+    Op::template segment<kRefetch>(a, lds, su, s, g, t_begin, t_end, kToSlot,
+                                   wg + static_cast<int64_t>(s) * hkv + g);
     u = seg_end;
   }
 }
@@ -752,87 +894,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Debug kernels: the same workgroup coordinates, partition / wave / block walk
-// and page walker as the split kernel.
+// Debug helper: fill an int64 buffer (the resolve test marks tokens past a
+// sequence with -1).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fill_i64_kernel(int64_t* p, int64_t n, int64_t value) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
     p[i] = value;
 }
 
-__global__ __launch_bounds__(kThreads) void debug_resolve_kernel(LaunchArgs a, int32_t kv_head,
-                                                                 int64_t* offs) {
-  const int lane = lane_id();
-  const int w = wave_id();
-  const SplitCoord c = split_coord(a);
-  if (c.g != kv_head) return;
-  const int seq_len = min(max(a.seq_lens[c.s], 0), a.max_seq_len);
-  const int t_begin = c.part * a.partition_tokens;
-  if (t_begin >= seq_len) return;
-  const int t_end = min(t_begin + a.partition_tokens, seq_len);
-  const int row_stride = a.num_kv_heads * kD;
-  int t = t_begin + w * kWaveTokens;
-  if (t >= t_end) return;
-  PageWalker walker;
-  walker.init(a.block_table + static_cast<int64_t>(c.s) * a.max_blocks, a.block_size, t,
-              PageWalker::pages_for(t_end, a.block_size), lane);
-  for (;;) {
-    const int nv = min(kWaveTokens, t_end - t);
-    const int64_t base = walker.base(a.k_page_stride, row_stride, c.g * kD);
-    if (lane < nv)
-      offs[static_cast<int64_t>(c.s) * a.max_seq_len + t + lane] =
-          base + static_cast<int64_t>(lane) * row_stride;
-    t += kTileTokens;
-    if (t >= t_end) break;
-    walker.advance<true>(kTileTokens, lane);
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void debug_gather_kernel(LaunchArgs a, int32_t which,
-                                                                uint16_t* dense) {
-  const int lane = lane_id();
-  const int w = wave_id();
-  const SplitCoord c = split_coord(a);
-  const int s = c.s, g = c.g;
-  const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
-  const int t_begin = c.part * a.partition_tokens;
-  if (t_begin >= seq_len) return;
-  const int t_end = min(t_begin + a.partition_tokens, seq_len);
-  const int row_stride = a.num_kv_heads * kD;
-  int t = t_begin + w * kWaveTokens;
-  if (t >= t_end) return;
-  PageWalker walker;
-  walker.init(a.block_table + static_cast<int64_t>(s) * a.max_blocks, a.block_size, t,
-              PageWalker::pages_for(t_end, a.block_size), lane);
-  for (;;) {
-    const int nv = min(kWaveTokens, t_end - t);
-    const int64_t base = walker.base(a.k_page_stride, row_stride, g * kD);
-    auto dense_row = [&](int i) {
-      return dense + ((static_cast<int64_t>(s) * a.max_seq_len + t + i) * a.num_kv_heads + g) * kD;
-    };
-    if (which == 0) {
-      KBlock kb;
-      load_k_block(a.k + base, row_stride * 2, k_lane_offset(lane, row_stride * 2), kb);
-      const int i = lane & 15;
-      if (i < nv) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          *reinterpret_cast<u32x4*>(dense_row(i) + 32 * ks + 8 * (lane >> 4)) = kb.r[ks];
-      }
-    } else {
-      VBlock vb;
-      load_v_block(a.k + base, row_stride * 2, nv - 1, lane, vb);
-#pragma unroll
-      for (int i = 0; i < kWaveTokens / 2; ++i) {
-        const int rr = v_row(i, lane);
-        if (rr < nv) *reinterpret_cast<u32x4*>(dense_row(rr) + 8 * (lane & 31)) = vb.r[i];
-      }
-    }
-    t += kTileTokens;
-    if (t >= t_end) break;
-    walker.advance<true>(kTileTokens, lane);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Bandwidth probes.
@@ -881,22 +950,48 @@ bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size) {
   return (partition_tokens + block_size - 1) / block_size + 1 > 64;
 }
 
-hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream) {
+namespace {
+
+template <class Op>
+hipError_t launch_fixed(const LaunchArgs& a, bool direct, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
   if (blocks == 0) return hipSuccess;
   const bool refetch = partition_needs_refetch(a.partition_tokens, a.block_size);
-  auto kern = direct ? (refetch ? split_decode_kernel<true, true> : split_decode_kernel<true, false>)
-                     : (refetch ? split_decode_kernel<false, true> : split_decode_kernel<false, false>);
+  auto kern = direct ? (refetch ? split_decode_kernel<Op, true, true>
+                                : split_decode_kernel<Op, true, false>)
+                     : (refetch ? split_decode_kernel<Op, false, true>
+                                : split_decode_kernel<Op, false, false>);
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, hipStream_t stream) {
+template <class Op>
+hipError_t launch_balanced(const LaunchArgs& a, bool refetch, hipStream_t stream) {
   if (a.num_seqs == 0 || a.balanced_grid == 0) return hipSuccess;
-  auto kern = refetch ? balanced_split_kernel<true> : balanced_split_kernel<false>;
+  auto kern = refetch ? balanced_split_kernel<Op, true> : balanced_split_kernel<Op, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(a.balanced_grid)), dim3(kThreads), 0, stream,
                      a);
   return hipGetLastError();
+}
+
+// The same split (fixed or balanced) with another Op.
+template <class Op>
+hipError_t launch_walk(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream) {
+  return c.balanced ? launch_balanced<Op>(a, c.refetch, stream)
+                    : launch_fixed<Op>(a, /*direct=*/false, stream);
+}
+
+}  // namespace
+
+hipError_t launch_split(const LaunchArgs& a, bool direct, bool k_rows, hipStream_t stream) {
+  return k_rows ? launch_fixed<DecodeOp<true>>(a, direct, stream)
+                : launch_fixed<DecodeOp<false>>(a, direct, stream);
+}
+
+hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,
+                                 hipStream_t stream) {
+  return k_rows ? launch_balanced<DecodeOp<true>>(a, refetch, stream)
+                : launch_balanced<DecodeOp<false>>(a, refetch, stream);
 }
 
 hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream) {
@@ -907,28 +1002,19 @@ hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream
   return hipGetLastError();
 }
 
-
-hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* offsets,
-                                hipStream_t stream) {
+hipError_t launch_debug_resolve(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(a.num_seqs) * a.max_seq_len;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_i64_kernel, dim3(256), dim3(256), 0, stream, offsets, total,
+  hipLaunchKernelGGL(fill_i64_kernel, dim3(256), dim3(256), 0, stream, a.dbg_offsets, total,
                      static_cast<int64_t>(-1));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
-  hipLaunchKernelGGL(debug_resolve_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
-                     stream, a, kv_head, offsets);
-  return hipGetLastError();
+  return launch_walk<DebugResolveOp>(a, c, stream);
 }
 
-hipError_t launch_debug_gather(const LaunchArgs& a, int32_t which, uint16_t* dense,
-                               hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(debug_gather_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0,
-                     stream, a, which, dense);
-  return hipGetLastError();
+hipError_t launch_debug_gather(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream) {
+  return c.k_rows ? launch_walk<DebugGatherOp<true>>(a, c, stream)
+                  : launch_walk<DebugGatherOp<false>>(a, c, stream);
 }
 
 int32_t probe_sink_floats() { return kProbeBlocks * 4; }

@@ -5,7 +5,17 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
+
+// pkv_decode and its workspace size (shared with the allocation-free entry
+// point, which passes its static scratch array as the workspace).
+size_t decode_workspace(const pkv_decode_params* params);
+pkv_status decode_call(const pkv_decode_params* params, const void* q, const void* key_cache,
+                       const void* value_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, void* out, float* out_f32, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 constexpr int kHeadSize = 256;   // D
 constexpr int kGroup = 6;        // query heads per KV head
@@ -37,19 +47,35 @@ struct LaunchArgs {
   int32_t max_seq_len;
   int32_t balanced_grid;  // balanced split: workgroups G (0 = fixed partitions)
   float scale_log2;     // scale * log2(e)
+  // debug walks only
+  int64_t* dbg_offsets;   // resolve: int64 [S, max_seq_len]
+  uint16_t* dbg_dense;    // gather: bf16 [S, max_seq_len, Hkv, D]
+  int32_t dbg_kv_head;    // resolve: the KV head recorded
+  int32_t dbg_which;      // gather: 0 = the K loader, 1 = the V loader
+};
+
+// How a decode call splits its work: the balanced share or fixed partitions,
+// whether a segment may refetch its page list, and whether K is loaded as
+// whole rows and staged through LDS (else straight into the MFMA operand).
+struct SplitChoice {
+  bool balanced;
+  bool refetch;
+  bool k_rows;
 };
 
 // split kernel: per (sequence, KV head, partition). direct=true writes the
 // final bf16 (and optional fp32) output, valid only when n_parts == 1.
-hipError_t launch_split(const LaunchArgs& a, bool direct, hipStream_t stream);
+hipError_t launch_split(const LaunchArgs& a, bool direct, bool k_rows, hipStream_t stream);
 // balanced split: G = a.balanced_grid workgroups share the tiles evenly.
-hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, hipStream_t stream);
+hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,
+                                 hipStream_t stream);
 hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream);
 bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size);
-hipError_t launch_debug_resolve(const LaunchArgs& a, int32_t kv_head, int64_t* offsets,
-                                hipStream_t stream);
-hipError_t launch_debug_gather(const LaunchArgs& a, int32_t which, uint16_t* dense,
-                               hipStream_t stream);
+// The split `c` walks its segments and records what decode reads: row
+// offsets (a.dbg_offsets, a.dbg_kv_head) or rows through decode's loaders
+// (a.dbg_dense, a.dbg_which).
+hipError_t launch_debug_resolve(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream);
+hipError_t launch_debug_gather(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream);
 // KV append: one wave per new token, rows moved as 16-byte chunks.
 struct AppendArgs {
   const uint16_t* k_new;

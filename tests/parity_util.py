@@ -36,6 +36,34 @@ def oracle_case(case, seqs=None):
     return o, lse
 
 
+def oracle_case_parallel(case, seqs=None, workers=None):
+    """oracle_case with the sequences spread over host threads (numpy releases
+    the GIL in its loops; BLAS is held to one thread per worker)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    seqs = list(range(case.num_seqs) if seqs is None else seqs)
+    q = f64(case.q)
+    o = np.zeros(q.shape)
+    lse = np.zeros(q.shape[:2])
+    if workers is None:
+        try:
+            workers = len(os.sched_getaffinity(0))
+        except AttributeError:
+            workers = os.cpu_count() or 1
+        workers = max(1, min(16, workers, len(seqs)))
+
+    def one(s):
+        o[s], lse[s] = od.attention_decode(q[s], f64(case.keys(s)), f64(case.values(s)),
+                                           case.scale)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, seqs))
+    return o, lse
+
+
 def assert_bf16_close(out: torch.Tensor, ref: np.ndarray, rows=None, what=""):
     got = f64(out)
     if rows is not None:

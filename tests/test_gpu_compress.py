@@ -148,10 +148,9 @@ def test_compress_workloads(name):
     print(f"[gpu] compress workload {name}", flush=True)
     case = synth.make_compress_case(name, device="cuda")
     out = run(case)
-    n = case.num_outputs
-    rng = np.random.default_rng(0)
-    sample = sorted(set([0, 1, n // 2, n - 2, n - 1] + list(rng.integers(0, n, size=11))))
-    check(case, out, outputs=sample if n > 256 else None, what=name)
+    worst = check(case, out, what=name)   # every output
+    print(f"[gpu] {name}: {case.num_outputs} outputs, worst error / bound {worst:.3f}",
+          flush=True)
 
 
 def test_compress_splits_and_block_shuffles():

@@ -9,7 +9,8 @@ import torch
 import paged_kv_cache_36_amd as pkv
 from oracle import decode as od
 from paged_kv_cache_36_amd import synth
-from tests.parity_util import (assert_bf16_close, assert_rows_rel, bits, f64, oracle_case)
+from tests.parity_util import (assert_bf16_close, assert_rows_rel, bits, f64, oracle_case,
+                               oracle_case_parallel)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,25 +42,58 @@ def params_of(case, partition_tokens=0):
 
 # ------------------------------------------------------------ addressing (bit-exact)
 
+def check_resolve(case, prm, heads=range(4)):
+    table = case.block_table.cpu().numpy()
+    for g in heads:
+        got = pkv.debug_resolve(prm, g, case.block_table, case.seq_lens).cpu().numpy()
+        ref = od.resolve_offsets(table, case.lens, case.block_size, case.k_cache.stride(0), 4,
+                                 256, g, prm.max_seq_len)
+        assert np.array_equal(got, ref), (case.name, prm.partition_tokens, g)
+        yield got
+
+
+# The debug walks run the split pkv_decode would run for the same params:
+# fixed partitions for P != 0 or one sequence, the balanced split for P = 0
+# with several sequences.
 @pytest.mark.parametrize("bsz", [16, 64, 784, 832])
 @pytest.mark.parametrize("ptok", [64, 256, 0])
 def test_resolver_offsets_bit_exact(bsz, ptok):
     case = synth.build_case(f"res{bsz}", lens=[1, 63, 65, 785, 1700, 833], block_size=bsz,
                             seed=11, device="cuda")
     prm = params_of(case, ptok)
-    for g in range(4):
-        got = pkv.debug_resolve(prm, g, case.block_table, case.seq_lens).cpu().numpy()
-        ref = od.resolve_offsets(case.block_table.cpu().numpy(), case.lens, bsz,
-                                 case.k_cache.stride(0), 4, 256, g, case.max_seq_len)
-        assert np.array_equal(got, ref), (bsz, ptok, g)
+    assert pkv.plan(prm)["balanced"] == (1 if ptok == 0 else 0)
+    for _ in check_resolve(case, prm):
+        pass
+    one = synth.build_case(f"res1_{bsz}", lens=[1700], block_size=bsz, seed=14, device="cuda")
+    for _ in check_resolve(one, params_of(one, ptok)):
+        pass
 
 
-@pytest.mark.parametrize("which", [0, 1])
-@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
-def test_tile_loaders_gather_bit_exact(which, bsz):
-    case = synth.build_case(f"gat{bsz}", lens=[70, 1, 1600, 832], block_size=bsz, seed=12,
+def test_resolver_balanced_page_list_refetch():
+    # 16-token pages and runs longer than 64 pages: the balanced walker
+    # refetches its page list inside the loop
+    case = synth.build_case("resrf", lens=[150000, 70000, 333], block_size=16, seed=15,
                             device="cuda")
-    prm = params_of(case, 256)
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    for _ in check_resolve(case, prm, heads=[0, 3]):
+        pass
+
+
+def test_resolver_wide_pool_past_2_31_elements():
+    # The wide batch's pool holds about 2.4e9 elements per cache, so row
+    # offsets pass 2^31: every token's offset for all 4 KV heads, through the
+    # split pkv_decode runs for this workload (fixed 4096-token partitions)
+    case = synth.make_case("wide_64seq_b832_p4096", device="cuda")
+    prm = params_of(case, case.partition_tokens)
+    top = 0
+    for got in check_resolve(case, prm):
+        top = max(top, int(got.max()))
+    assert top > 2 ** 31, top
+    print(f"[gpu] wide pool: largest row offset {top} elements (2^31 = {2 ** 31})", flush=True)
+
+
+def check_gather(case, prm, which):
     sentinel = 0x1234
     dense = pkv.debug_gather(prm, which, case.k_cache, case.block_table, case.seq_lens,
                              fill=sentinel)
@@ -67,8 +101,22 @@ def test_tile_loaders_gather_bit_exact(which, bsz):
     d = bits(dense)
     for s in range(case.num_seqs):
         n = case.lens[s]
-        assert np.array_equal(d[s, :n], bits(case.keys(s))), (which, bsz, s)
+        assert np.array_equal(d[s, :n], bits(case.keys(s))), (which, case.block_size, s)
         assert np.all(d[s, n:] == sentinel)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("bsz", [16, 64, 784, 832])
+def test_tile_loaders_gather_bit_exact(which, bsz):
+    # a batch (K as whole rows), with fixed partitions and with the balanced
+    # split, and one sequence (K in the MFMA operand layout)
+    case = synth.build_case(f"gat{bsz}", lens=[70, 1, 1600, 832], block_size=bsz, seed=12,
+                            device="cuda")
+    for ptok in (256, 0):
+        check_gather(case, params_of(case, ptok), which)
+    one = synth.build_case(f"gat1_{bsz}", lens=[1601], block_size=bsz, seed=13, device="cuda")
+    for ptok in (256, 0):
+        check_gather(one, params_of(one, ptok), which)
 
 
 def test_joint_kv_unbind_view_addressing():
@@ -225,24 +273,27 @@ def test_page784_vs_page832_ab():
 
 def test_batched_long_context_workload():
     case = synth.make_case("batched_8seq_t131072_b832", device="cuda")
-    out = run_decode(case)
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    out = run_decode(case, out_f32=out32)
     print(f"[gpu] batched plan {pkv.plan(params_of(case))}", flush=True)
-    assert_bf16_close(out, oracle_case(case)[0], what="batched")
+    ref, _ = oracle_case_parallel(case)
+    assert_bf16_close(out, ref, what="batched")
+    assert_rows_rel(f64(out32), ref, what="batched fp32")
 
 
-def test_wide_serving_batch_sampled():
+def test_wide_serving_batch_every_sequence():
+    # all 64 sequences (about 2.2 M tokens) against the oracle, which runs on
+    # the host's cores; bf16 output elementwise and the fp32 output per row
     case = synth.make_case("wide_64seq_b832_p4096", device="cuda")
     assert case.partition_tokens == 4096
-    out = run_decode(case)
-    o = f64(out)
-    assert np.all(np.isfinite(o))
-    lens = np.array(case.lens)
-    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 17, 40, 63})
-    q = f64(case.q)
-    for s in picks:
-        ref, _ = od.attention_decode(q[s], f64(case.keys(s)), f64(case.values(s)), case.scale)
-        assert_bf16_close(out[s], ref, what=f"wide s={s} L={case.lens[s]}")
-    print(f"[gpu] wide checked seqs {picks}", flush=True)
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    out = run_decode(case, out_f32=out32)
+    print(f"[gpu] wide: {case.num_seqs} sequences, {sum(case.lens)} tokens, oracle on host",
+          flush=True)
+    ref, _ = oracle_case_parallel(case)
+    assert_bf16_close(out, ref, what="wide")
+    worst = assert_rows_rel(f64(out32), ref, what="wide fp32")
+    print(f"[gpu] wide: worst fp32 row rel err {worst:.2e}", flush=True)
 
 
 # ------------------------------------------------------------ balanced split
