@@ -47,6 +47,7 @@ struct Plan {
   int32_t grid = 0;         // balanced: workgroups G
   bool refetch = false;     // a segment may span more than the walker's 64 page ids
   bool k_rows = false;      // K loaded as whole rows and staged through LDS
+  bool ordered = false;     // fixed partitions taken full ones first, tails last
   size_t o_part_bytes = 0;
   size_t lse_bytes = 0;
   size_t workspace = 0;
@@ -100,6 +101,11 @@ Plan make_fixed_plan(const pkv_decode_params* p) {
   pl.n_parts = p->max_seq_len > 0 ? (p->max_seq_len + P - 1) / P : 1;
   pl.refetch = pkv::partition_needs_refetch(P, p->block_size);
   pl.k_rows = k_rows_for(p);
+  // Several sequences of several partitions each: the dispatch order of
+  // ordered_coord (full partitions first, the shorter last ones at the end,
+  // no empty workgroups among the live ones). It needs the lengths before
+  // the first loads, which one sequence's short decode cannot afford.
+  pl.ordered = p->num_seqs > 1 && p->num_seqs <= pkv::kMaxOrderedSeqs && pl.n_parts > 1;
   if (pl.n_parts > 1) {
     const size_t rows = static_cast<size_t>(p->num_seqs) * p->num_q_heads * pl.n_parts;
     pl.o_part_bytes = round_up(rows * pkv::kHeadSize * sizeof(float), kWorkspaceAlign);
@@ -169,12 +175,13 @@ void log_plan(const char* what, const pkv_decode_params* p, const Plan& pl) {
   if (!log_enabled()) return;
   std::fprintf(stderr,
                "[pkv] %s: S=%d Hq=%d Hkv=%d D=%d block_size=%d (64-token groups %d, tail %d) "
-               "max_seq_len=%d %s P=%d partitions=%d split_wg=%lld refetch=%d combine=%s "
-               "workspace=%zu\n",
+               "max_seq_len=%d %s P=%d partitions=%d split_wg=%lld refetch=%d k_rows=%d "
+               "ordered=%d combine=%s workspace=%zu\n",
                what, p->num_seqs, p->num_q_heads, p->num_kv_heads, p->head_size, p->block_size,
                p->block_size / 64, p->block_size % 64, p->max_seq_len,
                pl.balanced ? "balanced" : "fixed", pl.P, pl.n_parts,
                static_cast<long long>(split_workgroups(p, pl)), pl.refetch ? 1 : 0,
+               pl.k_rows ? 1 : 0, pl.ordered ? 1 : 0,
                (pl.balanced || pl.n_parts > 1) ? "yes" : "no", pl.workspace);
 }
 
@@ -193,6 +200,7 @@ pkv::SplitChoice split_choice(const Plan& pl) {
   c.balanced = pl.balanced;
   c.refetch = pl.refetch;
   c.k_rows = pl.k_rows;
+  c.ordered = pl.ordered;
   return c;
 }
 
@@ -300,10 +308,10 @@ pkv_status decode_call(const pkv_decode_params* params, const void* q, const voi
   a.out_f32 = out_f32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!pl.balanced && pl.n_parts == 1)
-    return hip_status(pkv::launch_split(a, /*direct=*/true, pl.k_rows, s));
+    return hip_status(pkv::launch_split(a, /*direct=*/true, split_choice(pl), s));
   carve_workspace(pl, workspace, a);
   st = pl.balanced ? hip_status(pkv::launch_balanced_split(a, pl.refetch, pl.k_rows, s))
-                   : hip_status(pkv::launch_split(a, /*direct=*/false, pl.k_rows, s));
+                   : hip_status(pkv::launch_split(a, /*direct=*/false, split_choice(pl), s));
   if (st != PKV_OK) return st;
   return hip_status(pkv::launch_combine(a, pl.balanced, s));
 }
@@ -430,7 +438,7 @@ pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
   a.out = static_cast<uint16_t*>(out);
   a.out_f32 = out_f32;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(pkv::launch_split(a, /*direct=*/false, pl.k_rows, s));
+  st = hip_status(pkv::launch_split(a, /*direct=*/false, split_choice(pl), s));
   if (st != PKV_OK) return st;
   return hip_status(pkv::launch_combine(a, /*balanced=*/false, s));
 }
@@ -457,7 +465,7 @@ pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void*
   a.o_part = o_partial;
   a.lse_part = lse_partial;
   return hip_status(
-      pkv::launch_split(a, /*direct=*/false, pl.k_rows, static_cast<hipStream_t>(stream)));
+      pkv::launch_split(a, /*direct=*/false, split_choice(pl), static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,

@@ -359,6 +359,67 @@ __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
   return c;
 }
 
+// Workgroup coordinates of a fixed-partition launch in dispatch order (the
+// grid is dispatched in workgroup order): first every full partition (s, p),
+// (p + 1) P <= L_s, in (s, p) order, then the last, shorter partition of
+// every sequence whose length is not a multiple of P, in sequence order; the
+// workgroups after those have no partition and return false. So the grid
+// ends with its shortest partitions instead of with whatever partitions the
+// last sequences have, and the slots of partitions past a sequence's end are
+// not interleaved with live ones. The KV head stays fastest. Wave 0 counts
+// the full and the tail partitions per sequence from seq_lens (prefix sums in
+// LDS, chunks of 64 sequences); every workgroup does this itself.
+__device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full_pref,
+                                              int32_t* tail_pref, SplitCoord& c) {
+  const int S = a.num_seqs;
+  const int P = a.partition_tokens;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry_f = 0, carry_t = 0;
+    if (lane == 0) full_pref[0] = tail_pref[0] = 0;
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int si = c0 + lane;
+      const int len = si < S ? min(max(a.seq_lens[si], 0), a.max_seq_len) : 0;
+      int f = len / P;
+      int t = (len - f * P) > 0 ? 1 : 0;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        const int uf = __shfl_up(f, sh);
+        const int ut = __shfl_up(t, sh);
+        if (lane >= sh) {
+          f += uf;
+          t += ut;
+        }
+      }
+      if (si < S) {
+        full_pref[si + 1] = carry_f + f;
+        tail_pref[si + 1] = carry_t + t;
+      }
+      carry_f += __shfl(f, 63);
+      carry_t += __shfl(t, 63);
+    }
+  }
+  __syncthreads();
+  int bid = blockIdx.x;
+  c.g = bid % a.num_kv_heads;
+  const int item = bid / a.num_kv_heads;
+  const int n_full = full_pref[S];
+  const int32_t* pref = item < n_full ? full_pref : tail_pref;
+  const int k = item < n_full ? item : item - n_full;
+  if (k >= pref[S]) return false;
+  // the last s with pref[s] <= k (uniform search)
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid] <= k) lo = mid; else hi = mid;
+  }
+  c.s = lo;
+  // a full partition's index within its sequence, or the tail's: the count
+  // of full partitions of s
+  c.part = item < n_full ? k - full_pref[lo] : full_pref[lo + 1] - full_pref[lo];
+  return true;
+}
+
 // LDS of one split workgroup.
 template <bool kKRows>
 struct SplitLds {
@@ -658,11 +719,21 @@ struct DebugGatherOp {
 // kRefetch: the partition may span more than 64 pages (pages smaller than
 // P / 63 tokens), so the page list is refetched inside the loop; chosen on
 // the host from P and the block size.
+// kOrdered: the workgroups take the partitions in the order of
+// ordered_coord (several sequences, several partitions each); otherwise in
+// grid order (sequence, partition, KV head), whose page list and q loads go
+// out before the sequence length arrives.
 // ---------------------------------------------------------------------------
-template <class Op, bool kDirect, bool kRefetch>
+template <class Op, bool kDirect, bool kRefetch, bool kOrdered>
 __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a) {
   __shared__ __attribute__((aligned(16))) typename Op::Lds lds;
-  const SplitCoord c = split_coord(a);
+  SplitCoord c;
+  if (kOrdered) {
+    __shared__ int32_t full_pref[kMaxOrderedSeqs + 1], tail_pref[kMaxOrderedSeqs + 1];
+    if (!ordered_coord(a, full_pref, tail_pref, c)) return;
+  } else {
+    c = split_coord(a);
+  }
   const int t_begin = c.part * a.partition_tokens;
   // the partition's pages as far as max_seq_len reaches (host-checked to fit
   // the table row), so the page list needs no sequence length
@@ -953,14 +1024,18 @@ bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size) {
 namespace {
 
 template <class Op>
-hipError_t launch_fixed(const LaunchArgs& a, bool direct, hipStream_t stream) {
+hipError_t launch_fixed(const LaunchArgs& a, bool direct, bool ordered, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
   if (blocks == 0) return hipSuccess;
   const bool refetch = partition_needs_refetch(a.partition_tokens, a.block_size);
-  auto kern = direct ? (refetch ? split_decode_kernel<Op, true, true>
-                                : split_decode_kernel<Op, true, false>)
-                     : (refetch ? split_decode_kernel<Op, false, true>
-                                : split_decode_kernel<Op, false, false>);
+  // the ordered coordinates only apply to partials (several partitions)
+  ordered = ordered && !direct && a.num_seqs <= kMaxOrderedSeqs;
+  auto kern = direct ? (refetch ? split_decode_kernel<Op, true, true, false>
+                                : split_decode_kernel<Op, true, false, false>)
+            : ordered ? (refetch ? split_decode_kernel<Op, false, true, true>
+                                 : split_decode_kernel<Op, false, false, true>)
+                      : (refetch ? split_decode_kernel<Op, false, true, false>
+                                 : split_decode_kernel<Op, false, false, false>);
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -978,14 +1053,15 @@ hipError_t launch_balanced(const LaunchArgs& a, bool refetch, hipStream_t stream
 template <class Op>
 hipError_t launch_walk(const LaunchArgs& a, const SplitChoice& c, hipStream_t stream) {
   return c.balanced ? launch_balanced<Op>(a, c.refetch, stream)
-                    : launch_fixed<Op>(a, /*direct=*/false, stream);
+                    : launch_fixed<Op>(a, /*direct=*/false, c.ordered, stream);
 }
 
 }  // namespace
 
-hipError_t launch_split(const LaunchArgs& a, bool direct, bool k_rows, hipStream_t stream) {
-  return k_rows ? launch_fixed<DecodeOp<true>>(a, direct, stream)
-                : launch_fixed<DecodeOp<false>>(a, direct, stream);
+hipError_t launch_split(const LaunchArgs& a, bool direct, const SplitChoice& c,
+                        hipStream_t stream) {
+  return c.k_rows ? launch_fixed<DecodeOp<true>>(a, direct, c.ordered, stream)
+                  : launch_fixed<DecodeOp<false>>(a, direct, c.ordered, stream);
 }
 
 hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,

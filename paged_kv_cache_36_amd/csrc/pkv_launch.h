@@ -23,6 +23,7 @@ constexpr int kWaveTokens = 16;  // tokens one wave handles per step (MFMA rows)
 constexpr int kWaves = 4;        // waves per split workgroup
 constexpr int kTileTokens = kWaveTokens * kWaves;  // 64 tokens per workgroup step
 constexpr int kMaxBalancedSeqs = 4096;             // sequences the balanced split handles
+constexpr int kMaxOrderedSeqs = 1024;              // sequences the ordered fixed split handles
 
 // Everything a split/combine/debug launch needs, already validated.
 struct LaunchArgs {
@@ -61,11 +62,13 @@ struct SplitChoice {
   bool balanced;
   bool refetch;
   bool k_rows;
+  bool ordered;   // fixed partitions in the ordered dispatch order
 };
 
 // split kernel: per (sequence, KV head, partition). direct=true writes the
 // final bf16 (and optional fp32) output, valid only when n_parts == 1.
-hipError_t launch_split(const LaunchArgs& a, bool direct, bool k_rows, hipStream_t stream);
+hipError_t launch_split(const LaunchArgs& a, bool direct, const SplitChoice& c,
+                        hipStream_t stream);
 // balanced split: G = a.balanced_grid workgroups share the tiles evenly.
 hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,
                                  hipStream_t stream);
