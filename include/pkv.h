@@ -23,7 +23,8 @@
  *    synchronizes the stream or the device.
  *  - The caller owns and allocates every buffer; the library allocates no
  *    device memory and keeps no state besides an immutable per-process log
- *    flag, so calls are thread-safe.
+ *    flag, so calls are thread-safe. (The one exception, pkv_decode_noalloc,
+ *    uses a static device array of its own; see there.)
  *  - Host-side checks run before any launch and return a negative status;
  *    a failed launch returns PKV_ERR_HIP. Nothing is written on error.
  *  - Preconditions that live in device memory are documented, not checked:
@@ -60,7 +61,9 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = -6, /* head_size != 256, group size != 6, or the call does
                                not apply to this plan                             */
   PKV_ERR_HIP = -7,         /* a HIP launch or runtime call failed                */
-  PKV_ERR_STRIDE = -8       /* page stride too small or not a multiple of 8       */
+  PKV_ERR_STRIDE = -8,      /* page stride too small or not a multiple of 8       */
+  PKV_ERR_SCRATCH = -9      /* pkv_decode_noalloc: the call needs more workspace
+                               than the static scratch array holds                */
 } pkv_status;
 
 /* Geometry of one decode call. All sizes in elements unless noted. */
@@ -207,6 +210,27 @@ PKV_API pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv
 PKV_API pkv_status pkv_debug_gather(const pkv_decode_params* params, int32_t which,
                             const void* cache, const int32_t* block_table,
                             const int32_t* seq_lens, void* dense, void* stream);
+
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Computes exactly what pkv_decode computes, with the same plan
+ * and kernels (bit-identical outputs), but takes no workspace: the partials
+ * (and the balanced split's tile prefix sums) go to a file-scope device array
+ * of PKV_NOALLOC_SCRATCH_BYTES bytes in the library, one per GPU, held from
+ * the first call on that GPU until the process ends. The call allocates
+ * nothing and needs no zeroed memory (everything it reads there it wrote in
+ * the same call). A call whose plan needs more workspace than the array
+ * holds (pkv_decode_workspace_bytes(params) > PKV_NOALLOC_SCRATCH_BYTES)
+ * returns PKV_ERR_SCRATCH before any GPU call; other errors are pkv_decode's.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller; calls on one stream are ordered. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+PKV_API size_t pkv_noalloc_scratch_bytes(void);
+PKV_API pkv_status pkv_decode_noalloc(const pkv_decode_params* params, const void* q,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* out, float* out_f32, void* stream);
 
 /* Bandwidth probes (used to calibrate measurements, not part of decode):
  * pkv_probe_read streams `bytes` (multiple of 16, 16-byte aligned) from `buf`

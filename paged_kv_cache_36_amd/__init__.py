@@ -24,8 +24,10 @@ from .api import (  # noqa: F401
     debug_gather,
     debug_resolve,
     decode,
+    decode_noalloc,
     decode_partials,
     make_params,
+    noalloc_scratch_bytes,
     page_tokens,
     plan,
     prefill,

@@ -138,6 +138,25 @@ def decode(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, 
     return out
 
 
+def noalloc_scratch_bytes() -> int:
+    return int(load().pkv_noalloc_scratch_bytes())
+
+
+def decode_noalloc(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, out, *,
+                   max_seq_len=None, partition_tokens=0, out_f32=None, stream=None):
+    """pkv_decode_noalloc: decode into the caller's ``out`` (bf16 [S, Hq, D])
+    and optional ``out_f32`` with the library's static scratch array as the
+    workspace; nothing is allocated on either side of the call."""
+    p = make_params(q, key_cache, value_cache, block_table, block_size, scale,
+                    max_seq_len, partition_tokens)
+    _seq_lens(seq_lens, q.shape[0])
+    _check(load().pkv_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(key_cache),
+                                     _ptr(value_cache), _ptr(block_table), _ptr(seq_lens),
+                                     _ptr(out), _ptr(out_f32), _stream(stream)),
+           "pkv_decode_noalloc")
+    return out
+
+
 def decode_partials(q, key_cache, value_cache, block_table, seq_lens, block_size, scale, *,
                     max_seq_len=None, partition_tokens=0, stream=None):
     """Returns (o_partial [S,Hq,n,D] f32, lse_partial [S,Hq,n] f32, out_f32 [S,Hq,D], out bf16)."""

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_append.hip", "pkv_prefill.hip", "pkv_compress.hip", "pkv_api.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_append.hip", "pkv_prefill.hip", "pkv_compress.hip",
+           "pkv_noalloc.hip", "pkv_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

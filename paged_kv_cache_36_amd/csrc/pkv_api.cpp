@@ -334,6 +334,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported head geometry (need head_size 256, 6 query heads per KV head)";
     case PKV_ERR_HIP: return "HIP launch or runtime error";
     case PKV_ERR_STRIDE: return "page stride smaller than a page or not a multiple of 8";
+    case PKV_ERR_SCRATCH:
+      return "workspace needed exceeds the static scratch array of pkv_decode_noalloc (32 MiB)";
     default: return "unknown status";
   }
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert b"gfx950" in lib.pkv_version()
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert lib.pkv_status_string(st) and lib.pkv_status_string(st) != b"unknown status"
     assert lib.pkv_status_string(42) == b"unknown status"
 
@@ -358,3 +358,24 @@ def test_prefill_validates_before_any_launch(lib):
         assert pf(ctypes.byref(q), fake, fake, fake, fake, fake, None, fake, need, None) == -4
     assert lib.pkv_prefill_key_splits(ctypes.byref(prefill_params(seq_len=100))) == -2
     assert lib.pkv_prefill_key_splits(None) == -1
+
+
+def test_noalloc_refuses_plans_beyond_its_array_without_a_gpu(lib):
+    # host-only path: the plan's workspace is compared with the static array
+    # before any HIP call, so this runs without a GPU (the pointers are never
+    # dereferenced)
+    cap = lib.pkv_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    big = params(num_seqs=4096, max_blocks_per_seq=79, max_seq_len=65536, partition_tokens=64)
+    assert lib.pkv_decode_workspace_bytes(ctypes.byref(big)) > cap
+    fake = ctypes.c_void_p(1 << 12)
+    st = lib.pkv_decode_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None, None)
+    assert st == -9
+    assert b"scratch" in lib.pkv_status_string(-9)
+    # invalid params report pkv_decode's own status first
+    bad = params(head_size=128)
+    assert lib.pkv_decode_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None,
+                                  None) == -6
+    # the wide batch's plan fits
+    wide = params(num_seqs=64, max_blocks_per_seq=79, max_seq_len=65536, partition_tokens=4096)
+    assert 0 < lib.pkv_decode_workspace_bytes(ctypes.byref(wide)) <= cap
