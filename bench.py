@@ -46,7 +46,10 @@ APPEND_WORKLOADS = {"append_decode_64tok_b832": (64, 832),
 # on a Hygon DCU (gfx936), same head layout, q = 1, page 832 (context only).
 PAGES_US = {"long_l8192_b832": 80.010, "long_l16384_b832": 122.411,
             "long_l32768_b832": 278.832}
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_36_amd", "csrc", "pkv_kernels.hip")
+# the decode kernels and the host plan that picks their variants: the recorded
+# traffic holds only while both are unchanged
+KERNEL_SRC = [os.path.join(ROOT, "paged_kv_cache_36_amd", "csrc", f)
+              for f in ("pkv_kernels.hip", "pkv_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_traffic.json")
 
 
@@ -55,8 +58,11 @@ def log(msg):
 
 
 def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
@@ -654,10 +660,11 @@ def main():
     main_res = measure(MAIN, args.steps, args.warmup, torch, pkv, synth)
     extra = []
     if args.workloads in ("all", "decode"):
-        caps = {"batched_8seq_t131072_b832": 200, "wide_64seq_b832_p4096": 20}
+        # the other decode workloads run 10-90 us per step: 200 replays at least, so the
+        # host-side synchronisation around the replay stays small against the timed work
         for name in EXTRA:
-            extra.append(measure(name, min(args.steps, caps.get(name, 400)), args.warmup,
-                                 torch, pkv, synth))
+            extra.append(measure(name, max(min(args.steps, 400), 200), args.warmup, torch, pkv,
+                                 synth))
     appends = []
     if args.workloads == "all":
         # one new token per sequence of the wide batch, and a 32768-token

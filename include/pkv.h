@@ -107,6 +107,12 @@ typedef struct {
   int32_t full_groups_per_page;  /* block_size / 64 (12 for 784, 13 for 832)       */
   int32_t tail_tokens_per_page;  /* block_size % 64 (16 for 784, 0 for 832)        */
   int64_t workspace_bytes;       /* what pkv_decode needs in `workspace`           */
+  int32_t k_rows;                /* 1: pkv_decode loads K as whole rows and stages
+                                    it through LDS (a batch); 0: straight into the
+                                    MFMA operand layout (one sequence)             */
+  int32_t ordered;               /* 1: pkv_decode's fixed partitions run in the
+                                    ordered dispatch (full partitions first, the
+                                    shorter last ones at the end)                  */
 } pkv_plan_info;
 
 /* Library version string (static storage). */

@@ -43,6 +43,8 @@ class PlanInfo(ctypes.Structure):
         ("full_groups_per_page", ctypes.c_int32),
         ("tail_tokens_per_page", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64),
+        ("k_rows", ctypes.c_int32),
+        ("ordered", ctypes.c_int32),
     ]
 
 

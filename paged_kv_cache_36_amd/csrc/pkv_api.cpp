@@ -320,7 +320,7 @@ pkv_status decode_call(const pkv_decode_params* params, const void* q, const voi
 
 extern "C" {
 
-const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+const char* pkv_version(void) { return "pkv 0.2.0 (gfx950)"; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -355,6 +355,8 @@ pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info) {
   info->full_groups_per_page = params->block_size / 64;
   info->tail_tokens_per_page = params->block_size % 64;
   info->workspace_bytes = static_cast<int64_t>(dec.workspace);
+  info->k_rows = dec.k_rows ? 1 : 0;
+  info->ordered = (!dec.balanced && dec.ordered) ? 1 : 0;
   return PKV_OK;
 }
 

@@ -418,51 +418,52 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   if (kh == 1 || !q_valid) return;
   // the max of both halves; -inf only when the query sees no key of this
   // workgroup's split (with one split, key 0 is visible to every query)
-  float mx = fmaxf(m, mbuf[kPfCols * kHeadSize + lane]);
+  const float m2 = mbuf[kPfCols * kHeadSize + lane];
+  const float l2 = mbuf[kPfCols * kHeadSize + 64 + lane];
+  float mx = fmaxf(m, m2);
   if (mx == -INFINITY) mx = 0.f;   // both halves empty: every weight stays 0
-  {
-    const float m2 = mbuf[kPfCols * kHeadSize + lane];
-    const float l2 = mbuf[kPfCols * kHeadSize + 64 + lane];
-    const float f1 = exp2_fast(m - mx), f2 = exp2_fast(m2 - mx);
-    lsum = lsum * f1 + l2 * f2;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * f1 + mbuf[(db * 16 + r) * 64 + lane] * f2;
-  }
+  const float f1 = exp2_fast(m - mx), f2 = exp2_fast(m2 - mx);
+  lsum = lsum * f1 + l2 * f2;
   // o = acc / l: register r of block db holds dim 32 db + 8 (r / 4) + 4 half + r % 4.
   // One split: lsum >= 1 (the maximum key has weight 1). Several: the split's
   // normalized partial and its log2-sum-exp, or 0 and -inf for no key.
+  // The halves are merged and written one block db at a time (a scheduling
+  // barrier per block), so only that block's 16 values from LDS are live
+  // next to the accumulator.
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float w1 = f1 * inv, w2 = f2 * inv;
+  float* orow_part = nullptr;
+  int64_t orow = 0;
   if constexpr (kSplit) {
     const int64_t prow = (static_cast<int64_t>(split) * a.num_q + qi) * hq + h;
     if (half == 0) a.lse_part[prow] = lsum > 0.f ? mx + __log2f(lsum) : -INFINITY;
-    float* orow = a.o_part + prow * kHeadSize + 4 * half;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * rq) =
-            f32x4{acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv, acc[db][4 * rq + 2] * inv,
-                  acc[db][4 * rq + 3] * inv};
-    return;
+    orow_part = a.o_part + prow * kHeadSize + 4 * half;
+  } else {
+    orow = (static_cast<int64_t>(qi) * hq + h) * kHeadSize + 4 * half;
   }
-  const int64_t orow = (static_cast<int64_t>(qi) * hq + h) * kHeadSize + 4 * half;
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < 8; ++db) {
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = acc[db][r] * w1 + mbuf[(db * 16 + r) * 64 + lane] * w2;
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const f32x4 o = {acc[db][4 * rq] * inv, acc[db][4 * rq + 1] * inv, acc[db][4 * rq + 2] * inv,
-                       acc[db][4 * rq + 3] * inv};
-      const int64_t idx = orow + 32 * db + 8 * rq;
-      if (a.out) {
-        u32x2 packed;
-        packed.x = f32_to_bf16(o.x) | (f32_to_bf16(o.y) << 16);
-        packed.y = f32_to_bf16(o.z) | (f32_to_bf16(o.w) << 16);
-        *reinterpret_cast<u32x2*>(a.out + idx) = packed;
+      const f32x4 v = {o[4 * rq], o[4 * rq + 1], o[4 * rq + 2], o[4 * rq + 3]};
+      if constexpr (kSplit) {
+        *reinterpret_cast<f32x4*>(orow_part + 32 * db + 8 * rq) = v;
+      } else {
+        const int64_t idx = orow + 32 * db + 8 * rq;
+        if (a.out) {
+          u32x2 packed;
+          packed.x = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+          packed.y = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+          *reinterpret_cast<u32x2*>(a.out + idx) = packed;
+        }
+        if (a.out_f32) *reinterpret_cast<f32x4*>(a.out_f32 + idx) = v;
       }
-      if (a.out_f32) *reinterpret_cast<f32x4*>(a.out_f32 + idx) = o;
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Merge of the key splits: one thread per (query, head, 4 dims);

@@ -379,3 +379,24 @@ def test_noalloc_refuses_plans_beyond_its_array_without_a_gpu(lib):
     # the wide batch's plan fits
     wide = params(num_seqs=64, max_blocks_per_seq=79, max_seq_len=65536, partition_tokens=4096)
     assert 0 < lib.pkv_decode_workspace_bytes(ctypes.byref(wide)) <= cap
+
+
+def test_plan_reports_k_layout_and_dispatch_order(lib):
+    # one sequence: K straight into the MFMA operand, grid order
+    st, info = plan(lib)
+    assert st == 0 and info.k_rows == 0 and info.ordered == 0
+    # the wide batch's shape: fixed 4096-token partitions, K rows, ordered
+    st, info = plan(lib, num_seqs=64, max_blocks_per_seq=79, max_seq_len=65536,
+                    partition_tokens=4096)
+    assert st == 0 and info.balanced == 0 and info.k_rows == 1 and info.ordered == 1
+    # a batch with the partition size left to the library: balanced, K rows
+    st, info = plan(lib, num_seqs=8, max_blocks_per_seq=40, max_seq_len=32768)
+    assert st == 0 and info.balanced == 1 and info.k_rows == 1 and info.ordered == 0
+    # one partition per sequence writes the output directly: no ordering
+    st, info = plan(lib, num_seqs=8, max_seq_len=4096, partition_tokens=4096)
+    assert st == 0 and info.num_partitions == 1 and info.ordered == 0
+    # past 1024 sequences fixed partitions keep the grid order
+    st, info = plan(lib, num_seqs=1025, max_seq_len=8192, partition_tokens=512)
+    assert st == 0 and info.ordered == 0
+    st, info = plan(lib, num_seqs=1024, max_seq_len=8192, partition_tokens=512)
+    assert st == 0 and info.ordered == 1

@@ -296,6 +296,44 @@ def test_wide_serving_batch_every_sequence():
     print(f"[gpu] wide: worst fp32 row rel err {worst:.2e}", flush=True)
 
 
+# ------------------------------------------------------------ fixed partitions, ordered
+
+def test_fixed_partitions_ordered_dispatch_edge_cases():
+    # More than 64 sequences (the per-workgroup prefix sums take several
+    # chunks), lengths that are exact multiples of P (no last partition),
+    # shorter than P (no full partition), empty, and one token.
+    rng = np.random.default_rng(81)
+    lens = [int(x) for x in rng.integers(0, 3000, size=300)]
+    lens[:8] = [0, 1, 512, 1024, 511, 513, 2048, 0]
+    case = synth.build_case("ord300", lens=lens, block_size=784, seed=81, device="cuda")
+    prm = params_of(case, 512)
+    info = pkv.plan(prm)
+    assert info["ordered"] == 1 and info["k_rows"] == 1 and info["balanced"] == 0
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    out = run_decode(case, 512, out_f32=out32)
+    live = [s for s, n in enumerate(lens) if n > 0]
+    ref, _ = oracle_case_parallel(case, seqs=live)
+    assert_bf16_close(out, ref, rows=live, what="ordered 300 seqs")
+    assert_rows_rel(f64(out32)[live], ref[live], what="ordered 300 seqs fp32")
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert np.all(f64(out)[s] == 0)
+    # the ordered walk, bit-exact
+    for _ in check_resolve(case, prm, heads=[1, 2]):
+        pass
+
+
+def test_fixed_partitions_beyond_the_ordered_limit_use_grid_order():
+    rng = np.random.default_rng(82)
+    lens = [int(x) for x in rng.integers(1, 700, size=1100)]
+    case = synth.build_case("grid1100", lens=lens, block_size=832, seed=82, device="cuda")
+    prm = params_of(case, 256)
+    assert pkv.plan(prm)["ordered"] == 0
+    out = run_decode(case, 256)
+    ref, _ = oracle_case_parallel(case)
+    assert_bf16_close(out, ref, what="grid order 1100 seqs")
+
+
 # ------------------------------------------------------------ balanced split
 
 def run_balanced(case, max_seq_len=None):
