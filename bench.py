@@ -49,7 +49,7 @@ PAGES_US = {"long_l8192_b832": 80.010, "long_l16384_b832": 122.411,
 # the decode kernels and the host plan that picks their variants: the recorded
 # traffic holds only while both are unchanged
 KERNEL_SRC = [os.path.join(ROOT, "paged_kv_cache_36_amd", "csrc", f)
-              for f in ("pkv_kernels.hip", "pkv_api.cpp")]
+              for f in ("pkv_kernels.hip", "pkv_plan.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_traffic.json")
 
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["pkv_kernels.hip", "pkv_append.hip", "pkv_prefill.hip", "pkv_compress.hip",
-           "pkv_noalloc.hip", "pkv_api.cpp"]
+           "pkv_noalloc.hip", "pkv_plan.cpp", "pkv_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
