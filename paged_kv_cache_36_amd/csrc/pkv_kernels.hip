@@ -362,15 +362,23 @@ __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
 // Workgroup coordinates of a fixed-partition launch in dispatch order (the
 // grid is dispatched in workgroup order): first every full partition (s, p),
 // (p + 1) P <= L_s, in (s, p) order, then the last, shorter partition of
-// every sequence whose length is not a multiple of P, in sequence order; the
+// every sequence whose length is not a multiple of P, longest first; the
 // workgroups after those have no partition and return false. So the grid
 // ends with its shortest partitions instead of with whatever partitions the
 // last sequences have, and the slots of partitions past a sequence's end are
 // not interleaved with live ones. The KV head stays fastest. Wave 0 counts
-// the full and the tail partitions per sequence from seq_lens (prefix sums in
-// LDS, chunks of 64 sequences); every workgroup does this itself.
+// the full and the last partitions per sequence from seq_lens (prefix sums in
+// LDS, chunks of 64 sequences); every workgroup does this itself. The last
+// partitions are ordered by a counting sort over kTailBuckets length buckets
+// (bucket 0 the longest; sequence order within a bucket), which only the
+// workgroups that take a last partition compute.
+constexpr int kTailBuckets = 64;
+__device__ __forceinline__ int tail_bucket(int r, int P) {   // 1 <= r < P
+  return static_cast<int>(static_cast<int64_t>(P - r) * kTailBuckets / P);
+}
 __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full_pref,
-                                              int32_t* tail_pref, SplitCoord& c) {
+                                              int32_t* tail_pref, int32_t* tail_sort,
+                                              SplitCoord& c) {
   const int S = a.num_seqs;
   const int P = a.partition_tokens;
   if (threadIdx.x < 64) {
@@ -404,19 +412,62 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
   c.g = bid % a.num_kv_heads;
   const int item = bid / a.num_kv_heads;
   const int n_full = full_pref[S];
-  const int32_t* pref = item < n_full ? full_pref : tail_pref;
-  const int k = item < n_full ? item : item - n_full;
-  if (k >= pref[S]) return false;
-  // the last s with pref[s] <= k (uniform search)
-  int lo = 0, hi = S;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pref[mid] <= k) lo = mid; else hi = mid;
+  if (item < n_full) {
+    // the last s with full_pref[s] <= item (uniform search)
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (full_pref[mid] <= item) lo = mid; else hi = mid;
+    }
+    c.s = lo;
+    c.part = item - full_pref[lo];
+    return true;
   }
-  c.s = lo;
-  // a full partition's index within its sequence, or the tail's: the count
-  // of full partitions of s
-  c.part = item < n_full ? k - full_pref[lo] : full_pref[lo + 1] - full_pref[lo];
+  const int k = item - n_full;   // the k-th longest last partition
+  if (k >= tail_pref[S]) return false;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    tail_sort[lane] = 0;   // the bucket counts (kTailBuckets == 64)
+    wave_lds_sync();
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int si = c0 + lane;
+      const int len = si < S ? min(max(a.seq_lens[si], 0), a.max_seq_len) : 0;
+      const int r = len - (len / P) * P;
+      if (r > 0) atomicAdd(&tail_sort[tail_bucket(r, P)], 1);
+    }
+    wave_lds_sync();
+    const int cnt = tail_sort[lane];
+    int incl = cnt;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int up = __shfl_up(incl, sh);
+      if (lane >= sh) incl += up;
+    }
+    const int start = incl - cnt;
+    // the one bucket holding position k, and k's place inside it
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(cnt > 0 && start <= k && k < incl);
+    const int b = static_cast<int>(__builtin_ctzll(hit));
+    int j = k - __shfl(start, b);
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int si = c0 + lane;
+      const int len = si < S ? min(max(a.seq_lens[si], 0), a.max_seq_len) : 0;
+      const int r = len - (len / P) * P;
+      const bool in = r > 0 && tail_bucket(r, P) == b;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(in);
+      const int n = __popcll(m);
+      if (j < n) {   // uniform: the j-th member of this chunk
+        const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32),
+            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0)));
+        if (in && below == j) tail_sort[kTailBuckets] = si;
+        break;
+      }
+      j -= n;
+    }
+  }
+  __syncthreads();
+  c.s = tail_sort[kTailBuckets];
+  c.part = min(max(a.seq_lens[c.s], 0), a.max_seq_len) / P;   // its full partitions
   return true;
 }
 
@@ -730,7 +781,8 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   SplitCoord c;
   if (kOrdered) {
     __shared__ int32_t full_pref[kMaxOrderedSeqs + 1], tail_pref[kMaxOrderedSeqs + 1];
-    if (!ordered_coord(a, full_pref, tail_pref, c)) return;
+    __shared__ int32_t tail_sort[kTailBuckets + 1];
+    if (!ordered_coord(a, full_pref, tail_pref, tail_sort, c)) return;
   } else {
     c = split_coord(a);
   }

@@ -1,4 +1,5 @@
-"""Every entry point the bench times under HIP graphs, replayed: each replay
+"""Every entry point the bench times (and the allocation-free decode) under HIP
+graphs, replayed: each replay
 must reproduce the eager result bit for bit, with unrelated eager work and
 synchronisations between the replays (the library records no memsets and
 allocates nothing, so a captured call is the same launches as an eager one).
@@ -52,7 +53,8 @@ def replay_matches(fn, outputs, replays=3, reset=None):
                 f"replay {r} differs from the eager result"
 
 
-@pytest.mark.parametrize("name", ["long_l8192_b832", "batched_8seq_t131072_b832"])
+@pytest.mark.parametrize("name", ["long_l8192_b832", "batched_8seq_t131072_b832",
+                                  "wide_64seq_b832_p4096"])
 def test_decode_graph_replays(name):
     print(f"[gpu] graph decode {name}", flush=True)
     case = synth.make_case(name, device="cuda")
@@ -66,6 +68,23 @@ def test_decode_graph_replays(name):
         pkv.decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
                    case.block_size, case.scale, max_seq_len=case.max_seq_len,
                    partition_tokens=case.partition_tokens, out=out, out_f32=out32, workspace=ws)
+
+    replay_matches(fn, [out, out32])
+
+
+def test_decode_noalloc_graph_replays():
+    # the allocation-free entry point is meant for callers that capture
+    # graphs: captured after one eager call, each replay gives its bits
+    print("[gpu] graph decode_noalloc", flush=True)
+    case = synth.build_case("gna", lens=[3000, 65, 1, 777], block_size=784, seed=33,
+                            device="cuda")
+    out = torch.empty_like(case.q)
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+
+    def fn():
+        pkv.decode_noalloc(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                           case.block_size, case.scale, out, max_seq_len=case.max_seq_len,
+                           out_f32=out32)
 
     replay_matches(fn, [out, out32])
 
