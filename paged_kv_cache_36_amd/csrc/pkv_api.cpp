@@ -18,7 +18,6 @@ namespace {
 
 using pkv::base_args;
 using pkv::check_params;
-using pkv::kPlanCUs;
 using pkv::kWorkspaceAlign;
 using pkv::make_decode_plan;
 using pkv::make_fixed_plan;
@@ -84,7 +83,7 @@ namespace {
 // splits a call may ask for, and the CU count the automatic choice fills.
 constexpr int64_t kPrefillQueries = 128;
 constexpr int32_t kPrefillMaxSplits = 64;
-constexpr int64_t kCus = kPlanCUs;
+// the CUs the automatic split count fills: pkv::plan_cus()
 
 // Host checks shared by the prefill entry points.
 pkv_status check_prefill_params(const pkv_prefill_params* p) {
@@ -114,13 +113,14 @@ int32_t prefill_key_splits(const pkv_prefill_params* p) {
   if (p->key_splits > 0) return p->key_splits;
   const int64_t nqb = (p->num_q_tokens + kPrefillQueries - 1) / kPrefillQueries;
   const int64_t wgs = nqb * p->num_q_heads;
-  if (wgs >= 2 * kCus) return 1;
+  const int64_t cus = pkv::plan_cus();
+  if (wgs >= 2 * cus) return 1;
   // keys of the shortest query block (block 0): up to its last query's position
   const int64_t kend0 = static_cast<int64_t>(p->seq_len) - p->num_q_tokens +
                         std::min<int64_t>(kPrefillQueries, p->num_q_tokens);
   const int64_t tiles0 = (kend0 + 63) / 64;
   int32_t k = 1;
-  while (k < 16 && wgs * k < 3 * kCus && tiles0 / (k + 1) >= 16) ++k;
+  while (k < 16 && wgs * k < 3 * cus && tiles0 / (k + 1) >= 16) ++k;
   return k;
 }
 
@@ -489,7 +489,8 @@ pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* k
 namespace {
 
 // Window parts per output: the caller's S, else the smallest power of two that
-// gives at least one workgroup per CU (256) while parts keep 16 rows or more.
+// gives at least one workgroup per CU (pkv::plan_cus(), 256 on MI355X) while
+// parts keep 16 rows or more.
 // Measured on MI355X over the 12 shapes (1/4/8 requests, C = 128/256/512):
 // more parts than that only add partials and the combine launch (4 x 32768
 // tokens, C = 128: 1 / 2 / 4 parts ran 24.6 / 29.2 / 32.2 us), and a target of
@@ -497,7 +498,6 @@ namespace {
 // must touch at most kCompressMaxBlocks logical blocks (its ids sit one per
 // lane), and an output has at most kCompressMaxSplits parts (the combine's
 // lanes). Returns a negative status for invalid params.
-constexpr int64_t kCompressTargetWorkgroups = 256;
 
 int32_t compress_splits(const pkv_compress_params* p) {
   if (!p) return PKV_ERR_NULL;
@@ -523,7 +523,8 @@ int32_t compress_splits(const pkv_compress_params* p) {
   } else {
     s = 1;
     while (blocks_touched(s) > pkv::kCompressMaxBlocks) s *= 2;
-    while (static_cast<int64_t>(p->num_outputs) * s < kCompressTargetWorkgroups &&
+    const int64_t target = pkv::plan_cus();
+    while (static_cast<int64_t>(p->num_outputs) * s < target &&
            (c + 2 * s - 1) / (2 * s) >= 16)
       s *= 2;
     if (s > c) s = c;

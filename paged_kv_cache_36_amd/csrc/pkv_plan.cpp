@@ -5,17 +5,20 @@
 
 #include "pkv_plan.h"
 
+#include <hip/hip_runtime_api.h>
+
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 namespace pkv {
 namespace {
 
 // Automatic partition size: about one (sequence, partition, KV head)
-// workgroup per CU for the longest sequence in every batch slot, between 64
-// and 1024 tokens. Measured on MI355X: fewer, longer partitions cost less in
-// per-workgroup start-up and in partials, as long as every CU gets work.
-constexpr int64_t kAutoTargetWorkgroups = 256;
+// workgroup per CU (plan_cus()) for the longest sequence in every batch slot,
+// between 64 and 1024 tokens. Measured on MI355X: fewer, longer partitions
+// cost less in per-workgroup start-up and in partials, as long as every CU
+// gets work.
 constexpr int32_t kAutoMinPartition = 64;
 constexpr int32_t kAutoMaxPartition = 1024;
 
@@ -26,6 +29,28 @@ constexpr int32_t kAutoMaxPartition = 1024;
 bool k_rows_for(const pkv_decode_params* p) { return p->num_seqs > 1; }
 
 }  // namespace
+
+int64_t plan_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int64_t cus[kMaxDevices] = {};
+  static bool no_device = false;
+  std::lock_guard<std::mutex> lock(mu);
+  if (no_device) return kDefaultCUs;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    no_device = true;
+    return kDefaultCUs;
+  }
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = static_cast<int>(kDefaultCUs);
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 pkv_status check_params(const pkv_decode_params* p) {
   if (p == nullptr) return PKV_ERR_NULL;
@@ -58,7 +83,8 @@ Plan make_fixed_plan(const pkv_decode_params* p) {
     // counting the longest sequence for every slot of the batch.
     const int64_t token_heads =
         static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * static_cast<int64_t>(p->max_seq_len);
-    int64_t want = (token_heads + kAutoTargetWorkgroups - 1) / kAutoTargetWorkgroups;
+    const int64_t target = plan_cus();
+    int64_t want = (token_heads + target - 1) / target;
     want = (want + 63) / 64 * 64;
     if (want < kAutoMinPartition) want = kAutoMinPartition;
     if (want > kAutoMaxPartition) want = kAutoMaxPartition;
@@ -100,7 +126,7 @@ Plan make_decode_plan(const pkv_decode_params* p) {
   // One workgroup per CU: each already keeps all of its first two blocks per
   // wave in flight, and a second workgroup per CU measured slower at every
   // batch size tried (more partials, no more bandwidth).
-  int64_t g = kPlanCUs;
+  int64_t g = plan_cus();
   if (g > t_max) g = t_max;
   pl.grid = static_cast<int32_t>(g);
   // longest run of one (sequence, KV head) a workgroup can get

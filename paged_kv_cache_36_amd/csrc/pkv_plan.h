@@ -11,9 +11,11 @@
 
 namespace pkv {
 
-// Balanced split (pkv_decode with partition_tokens == 0): G workgroups, about
-// 1-2 per CU of a 256-CU gfx950 part, never more than the tiles there can be.
-constexpr int64_t kPlanCUs = 256;
+// Compute units the plans fill: the current device's count, read once per
+// device; 256 (every gfx950 part: MI350X and MI355X) when no device can be
+// queried, as in host-only planning on a machine without a GPU.
+constexpr int64_t kDefaultCUs = 256;
+int64_t plan_cus();
 constexpr size_t kWorkspaceAlign = 256;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
