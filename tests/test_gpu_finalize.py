@@ -10,7 +10,8 @@ group exponent) may follow either. A RoPE output carries an absolute error of
 up to 16 u (|u cos| + |w sin|), which spans several bf16 steps where the sum
 cancels; any bf16 value within that band is accepted there. The test allows
 32 u, accepts exactly the values inside the band, and requires departures
-from the nearest value to stay rare (they are counted). Everything
+from the nearest value to stay rare (they are counted, printed, and capped at one
+per 50 000 values). Everything
 else (exponent bytes, codes, bf16 bits, the pad byte, slot placement, bytes
 left untouched) must match bit for bit.
 """
@@ -31,6 +32,10 @@ pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -24
 BAND = 32 * U
+# At most one admissible non-nearest value per ALT_PER values checked (and 3
+# in any case): they occur only inside the rounding band of a bf16 tie, which
+# random data hits rarely (0 or 1 per case on MI355X, out of up to 524 288).
+ALT_PER = 50000
 
 
 @pytest.fixture(autouse=True)
@@ -141,7 +146,7 @@ def run_case(n_out, c_scale, eps, n_pages, seed, slots=None, pc_rows=600, c=128)
 def test_finalize_bytes(n_out, c_scale, eps, seed):
     print(f"[gpu] finalize N={n_out} scale={c_scale} eps={eps}", flush=True)
     checked, alt = run_case(n_out, c_scale, eps, n_pages=max(8, n_out // 16 + 4), seed=seed)
-    cap = max(3, checked * 512 // 500)
+    cap = max(3, checked * 512 // ALT_PER)
     print(f"[gpu] finalize N={n_out}: {alt} admissible non-nearest values of {checked * 512} "
           f"checked (cap {cap})", flush=True)
     assert checked == n_out
@@ -209,7 +214,7 @@ def test_compress_then_finalize_end_to_end():
         pc = oc.rope_position(case.positions[b], 512)
         alt += check_output(out[page, po:po + 576], out[page, so:so + 8], comp64[j],
                             f64(weight), 1e-6, cs[pc].numpy())
-    cap = max(3, n * 512 // 500)
+    cap = max(3, n * 512 // ALT_PER)
     print(f"[gpu] compress + finalize: {alt} admissible non-nearest values of {n * 512} "
           f"checked (cap {cap})", flush=True)
     assert alt <= cap
