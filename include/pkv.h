@@ -23,8 +23,9 @@
  *    synchronizes the stream or the device.
  *  - The caller owns and allocates every buffer; the library allocates no
  *    device memory and keeps no state besides an immutable per-process log
- *    flag, so calls are thread-safe. (The one exception, pkv_decode_noalloc,
- *    uses a static device array of its own; see there.)
+ *    flag and each device's compute-unit count (read once, for planning), so
+ *    calls are thread-safe. (The one exception, pkv_decode_noalloc, uses a
+ *    static device array of its own; see there.)
  *  - Host-side checks run before any launch and return a negative status;
  *    a failed launch returns PKV_ERR_HIP. Nothing is written on error.
  *  - Preconditions that live in device memory are documented, not checked:
@@ -87,7 +88,9 @@ typedef struct {
   float scale;                /* softmax scale (1/sqrt(256) = 1/16 for D = 256)     */
 } pkv_decode_params;
 
-/* What a call with these params will launch (host-only query, no GPU use).
+/* What a call with these params will launch (host-only query, no GPU work;
+ * the grids are sized for the current device's compute units, 256 when no
+ * device can be queried).
  * pkv_decode with partition_tokens == 0 and more than one sequence uses the
  * balanced split: a fixed number of workgroups G share the batch's 64-token
  * tiles evenly, whatever the length mix, and each (sequence, KV head) run of
