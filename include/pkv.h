@@ -124,8 +124,9 @@ PKV_API const char* pkv_version(void);
 /* Human-readable name of a pkv_status value (static storage). */
 PKV_API const char* pkv_status_string(int status);
 
-/* Validate params and report the launch plan. Host only; never touches a GPU.
- * Returns the same status pkv_decode would return for these params. */
+/* Validate params and report the launch plan. Host only: launches nothing
+ * (it may read the current device's compute-unit count once). Returns the
+ * same status pkv_decode would return for these params. */
 PKV_API pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info);
 
 /* Bytes of device workspace pkv_decode needs for these params (0 when one

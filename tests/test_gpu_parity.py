@@ -296,6 +296,56 @@ def test_wide_serving_batch_every_sequence():
     print(f"[gpu] wide: worst fp32 row rel err {worst:.2e}", flush=True)
 
 
+# ------------------------------------------------------------ other KV head counts
+
+def heads_variant(case, hkv):
+    """The case's pages with hkv KV heads (6 query heads each): the first hkv
+    heads for hkv <= 4; for 8, the 4 heads followed by the same rows with
+    each head's dims reversed (a different, finite head). Returns (q, k_cache,
+    v_cache, keys(s), values(s)) with the same block table."""
+    def widen(t):
+        if hkv <= 4:
+            return t[..., :hkv, :].contiguous()
+        return torch.cat([t, t.flip(-1)], dim=-2).contiguous()
+    q = case.q[:, :6 * hkv].contiguous() if hkv <= 4 else torch.cat(
+        [case.q, case.q.flip(-1)], dim=1).contiguous()
+    return (q, widen(case.k_cache), widen(case.v_cache), lambda s: widen(case.keys(s)),
+            lambda s: widen(case.values(s)))
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 8])
+@pytest.mark.parametrize("ptok", [0, 256])
+def test_other_kv_head_counts(hkv, ptok):
+    # the balanced split (P = 0) and ordered fixed partitions, Hq = 6 Hkv
+    case = synth.build_case(f"hkv{hkv}", lens=[3000, 1, 833, 0, 2500], block_size=784,
+                            seed=85, device="cuda")
+    q, kc, vc, keys, values = heads_variant(case, hkv)
+    assert q.shape[1] == 6 * hkv and kc.shape[2] == hkv
+    out32 = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    out = pkv.decode(q, kc, vc, case.block_table, case.seq_lens, case.block_size, case.scale,
+                     partition_tokens=ptok, max_seq_len=case.max_seq_len, out_f32=out32)
+    torch.cuda.synchronize()
+    prm = pkv.make_params(q, kc, vc, case.block_table, case.block_size, case.scale,
+                          case.max_seq_len, ptok)
+    info = pkv.plan(prm)
+    assert info["balanced"] == (1 if ptok == 0 else 0)
+    qd = f64(q)
+    for s, n in enumerate(case.lens):
+        if n == 0:
+            assert np.all(f64(out)[s] == 0)
+            continue
+        ref, _ = od.attention_decode(qd[s], f64(keys(s)), f64(values(s)), case.scale)
+        assert_bf16_close(out[s], ref, what=f"Hkv={hkv} P={ptok} s={s}")
+        assert_rows_rel(f64(out32)[s], ref, what=f"Hkv={hkv} P={ptok} s={s} fp32")
+    # the walker with this row stride, bit-exact
+    table = case.block_table.cpu().numpy()
+    for g in range(hkv):
+        got = pkv.debug_resolve(prm, g, case.block_table, case.seq_lens).cpu().numpy()
+        ref = od.resolve_offsets(table, case.lens, case.block_size, kc.stride(0), hkv, 256, g,
+                                 case.max_seq_len)
+        assert np.array_equal(got, ref), (hkv, ptok, g)
+
+
 # ------------------------------------------------------------ fixed partitions, ordered
 
 def test_fixed_partitions_ordered_dispatch_edge_cases():
