@@ -145,6 +145,9 @@ def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
                            f"events {gpu_ms:.3f} ms, split {split_us:.3f} us")
 
     us_step = wall_s * 1e6 / steps
+    # after the timed region: five more replays of the same graph, their median
+    # (the repeat protocol of the decode microbenchmark; outside the K timed steps)
+    repeats = sorted(timed(g_step)[0] * 1e6 / steps for _ in range(5))
     kernel = "balanced_split_kernel" if balanced else "split_decode_kernel"
     res = {
         "workload": name, "num_seqs": case.num_seqs, "total_tokens": sum(case.lens),
@@ -155,6 +158,7 @@ def measure(name, steps, warmup, torch, pkv, synth, **case_overrides):
         "split_workgroups": plan["split_workgroups"], "cold_copies": copies, "steps": steps,
         "algorithmic_bytes": nbytes,
         "us_per_step": round(us_step, 3),
+        "us_per_step_median5": round(repeats[2], 3),
         "gpu_us_per_step": round(gpu_ms * 1e3 / steps, 3),
         "split_us": round(split_us, 3),
         "warm_us_per_step": round(warm_us, 3),
