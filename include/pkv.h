@@ -104,8 +104,11 @@ typedef struct {
   int32_t num_partitions;        /* ceil(max_seq_len / P), at least 1              */
   int32_t split_workgroups;      /* workgroups of pkv_decode's split launch: G, or
                                     S * Hkv * num_partitions                       */
-  int32_t combine_workgroups;    /* pkv_decode's combine launch (S * Hq * 4), or 0
-                                    when one fixed partition covers every sequence */
+  int32_t combine_workgroups;    /* pkv_decode's combine launch: S * Hq * 4 (one
+                                    wave per sequence, head and 64 dims), S * Hkv
+                                    for a balanced split of 256 or more (sequence,
+                                    KV head) runs (one wave per run), or 0 when one
+                                    fixed partition covers every sequence         */
   int32_t balanced;              /* 1 when pkv_decode uses the balanced split      */
   int32_t full_groups_per_page;  /* block_size / 64 (12 for 784, 13 for 832)       */
   int32_t tail_tokens_per_page;  /* block_size % 64 (16 for 784, 0 for 832)        */

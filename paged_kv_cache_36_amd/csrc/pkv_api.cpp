@@ -170,7 +170,7 @@ pkv_status decode_call(const pkv_decode_params* params, const void* q, const voi
   st = pl.balanced ? hip_status(pkv::launch_balanced_split(a, pl.refetch, pl.k_rows, s))
                    : hip_status(pkv::launch_split(a, /*direct=*/false, split_choice(pl), s));
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_combine(a, pl.balanced, s));
+  return hip_status(pkv::launch_combine(a, pl.balanced, pl.combine_per_run, s));
 }
 
 }  // namespace pkv
@@ -207,7 +207,9 @@ pkv_status pkv_plan(const pkv_decode_params* params, pkv_plan_info* info) {
   info->num_partitions = fx.n_parts;
   info->split_workgroups = static_cast<int32_t>(split_workgroups(params, dec));
   info->combine_workgroups =
-      (dec.balanced || dec.n_parts > 1) ? params->num_seqs * params->num_q_heads * 4 : 0;
+      (dec.balanced && dec.combine_per_run) ? params->num_seqs * params->num_kv_heads
+      : (dec.balanced || dec.n_parts > 1)   ? params->num_seqs * params->num_q_heads * 4
+                                            : 0;
   info->balanced = dec.balanced ? 1 : 0;
   info->full_groups_per_page = params->block_size / 64;
   info->tail_tokens_per_page = params->block_size % 64;
@@ -270,7 +272,8 @@ pkv_status pkv_combine_balanced(const pkv_decode_params* params, const int32_t* 
   a.out = static_cast<uint16_t*>(out);
   a.out_f32 = out_f32;
   carve_workspace(pl, const_cast<void*>(workspace), a);
-  return hip_status(pkv::launch_combine(a, /*balanced=*/true, static_cast<hipStream_t>(stream)));
+  return hip_status(pkv::launch_combine(a, /*balanced=*/true, pl.combine_per_run,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
@@ -301,7 +304,7 @@ pkv_status pkv_decode_partials(const pkv_decode_params* params, const void* q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(pkv::launch_split(a, /*direct=*/false, split_choice(pl), s));
   if (st != PKV_OK) return st;
-  return hip_status(pkv::launch_combine(a, /*balanced=*/false, s));
+  return hip_status(pkv::launch_combine(a, /*balanced=*/false, /*per_run=*/false, s));
 }
 
 pkv_status pkv_split(const pkv_decode_params* params, const void* q, const void* key_cache,
@@ -345,7 +348,8 @@ pkv_status pkv_combine(const pkv_decode_params* params, const float* o_partial,
   a.lse_part = const_cast<float*>(lse_partial);
   a.out = static_cast<uint16_t*>(out);
   a.out_f32 = out_f32;
-  return hip_status(pkv::launch_combine(a, /*balanced=*/false, static_cast<hipStream_t>(stream)));
+  return hip_status(pkv::launch_combine(a, /*balanced=*/false, /*per_run=*/false,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_debug_resolve(const pkv_decode_params* params, int32_t kv_head,

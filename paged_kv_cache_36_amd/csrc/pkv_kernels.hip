@@ -1017,6 +1017,84 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
 }
 
 // ---------------------------------------------------------------------------
+// Balanced combine for batches of many (sequence, KV head) runs: one wave per
+// run merges the partials of all 6 of its query heads (a run's partial slots
+// are the same for the 6 heads); lane l takes dims 4 l .. 4 l + 3 of each
+// head. With many sequences each run has one or two partials, and one wave
+// per (sequence, head, quarter) would spend its time starting waves and
+// waiting for one load each; here a wave does 6 rows per round trip. The
+// partials go in chunks of kGroupChunk, folded into a running maximum, weight
+// sum and weighted sum per head (the same update as combine_kernel).
+// ---------------------------------------------------------------------------
+constexpr int kGroupChunk = 2;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_group_kernel(LaunchArgs a) {
+  const int lane = lane_id();
+  const int s = blockIdx.x / a.num_kv_heads;
+  const int g = blockIdx.x - s * a.num_kv_heads;
+  const int seq_len = min(max(a.seq_lens[s], 0), a.max_seq_len);
+  const int n = tiles_of(seq_len);
+  const int64_t T = a.prefix[a.num_seqs];
+  const int64_t G = min(static_cast<int64_t>(a.balanced_grid), T);   // as in the split
+  const int64_t u_lo = static_cast<int64_t>(a.prefix[s]) + static_cast<int64_t>(g) * n;
+  const int64_t w_first = n > 0 ? u_lo * G / T : 0;
+  const int64_t w_last = n > 0 ? (u_lo + n - 1) * G / T : -1;
+  const int np = static_cast<int>(w_last - w_first + 1);
+  const int64_t slot0 = w_first + static_cast<int64_t>(s) * a.num_kv_heads + g;
+
+  float m_run[kG], den[kG];
+  f32x4 acc[kG];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    m_run[h] = -INFINITY;
+    den[h] = 0.f;
+    acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < np; k0 += kGroupChunk) {
+    f32x4 x[kGroupChunk][kG];
+    float ls[kGroupChunk][kG];
+#pragma unroll
+    for (int c = 0; c < kGroupChunk; ++c) {   // straight-line; k >= np reads partial k0
+      const int k = k0 + c < np ? k0 + c : k0;
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        const int64_t prow = (slot0 + k) * kG + h;
+        x[c][h] = *reinterpret_cast<const f32x4*>(a.o_part + prow * kD + 4 * lane);
+        ls[c][h] = a.lse_part[prow];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kGroupChunk; ++c) {
+      const bool ok = k0 + c < np;
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        const float l2 = ok ? ls[c][h] * kLog2e : -INFINITY;
+        const float m_new = fmaxf(m_run[h], l2);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;   // nothing seen yet: weights 0
+        const float r = exp2_fast(m_run[h] - m_ref);
+        const float w = exp2_fast(l2 - m_ref);
+        den[h] = den[h] * r + w;
+        acc[h] = acc[h] * r + w * x[c][h];
+        m_run[h] = m_new;
+      }
+    }
+  }
+  const int64_t head0 = static_cast<int64_t>(s) * a.num_kv_heads * kG + g * kG;
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    const f32x4 r = np > 0 ? acc[h] * (1.f / den[h]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t idx = (head0 + h) * kD + 4 * lane;
+    if (a.out) {
+      u32x2 packed;
+      packed.x = f32_to_bf16(r.x) | (f32_to_bf16(r.y) << 16);
+      packed.y = f32_to_bf16(r.z) | (f32_to_bf16(r.w) << 16);
+      *reinterpret_cast<u32x2*>(a.out + idx) = packed;
+    }
+    if (a.out_f32) *reinterpret_cast<f32x4*>(a.out_f32 + idx) = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Debug helper: fill an int64 buffer (the resolve test marks tokens past a
 // sequence with -1).
 // ---------------------------------------------------------------------------
@@ -1122,7 +1200,14 @@ hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,
                 : launch_balanced<DecodeOp<false>>(a, refetch, stream);
 }
 
-hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream) {
+hipError_t launch_combine(const LaunchArgs& a, bool balanced, bool per_run, hipStream_t stream) {
+  if (balanced && per_run) {
+    const int64_t runs = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+    if (runs == 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_group_kernel, dim3(static_cast<uint32_t>(runs)),
+                       dim3(kCombineThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG * 4;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(balanced ? combine_kernel<true> : combine_kernel<false>,

@@ -72,7 +72,9 @@ hipError_t launch_split(const LaunchArgs& a, bool direct, const SplitChoice& c,
 // balanced split: G = a.balanced_grid workgroups share the tiles evenly.
 hipError_t launch_balanced_split(const LaunchArgs& a, bool refetch, bool k_rows,
                                  hipStream_t stream);
-hipError_t launch_combine(const LaunchArgs& a, bool balanced, hipStream_t stream);
+// combine: per_run (balanced only) merges each (sequence, KV head) run's six
+// query heads in one wave; otherwise one wave per (sequence, head, quarter)
+hipError_t launch_combine(const LaunchArgs& a, bool balanced, bool per_run, hipStream_t stream);
 bool partition_needs_refetch(int32_t partition_tokens, int32_t block_size);
 // The split `c` walks its segments and records what decode reads: row
 // offsets (a.dbg_offsets, a.dbg_kv_head) or rows through decode's loaders

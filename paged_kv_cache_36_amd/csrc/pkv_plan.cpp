@@ -21,6 +21,8 @@ namespace {
 // gets work.
 constexpr int32_t kAutoMinPartition = 64;
 constexpr int32_t kAutoMaxPartition = 1024;
+// (sequence, KV head) runs from which the balanced combine takes one wave per run
+constexpr int64_t kCombinePerRunMin = 256;
 
 // K load layout. Whole rows (full 128-byte lines, staged through LDS for the
 // MFMA operand) stream faster than the operand layout's half-line reads, at
@@ -135,6 +137,11 @@ Plan make_decode_plan(const pkv_decode_params* p) {
   pl.refetch = partition_needs_refetch(static_cast<int32_t>((seg_tokens + 63) / 64 * 64),
                                             p->block_size);
   pl.k_rows = k_rows_for(p);
+  // Many (sequence, KV head) runs: each has one or two partials, and one
+  // combine wave per run (its 6 heads) starts a fraction of the waves of one
+  // per (sequence, head, quarter). Few runs keep the finer combine, whose
+  // waves then have more partials each to load in parallel.
+  pl.combine_per_run = static_cast<int64_t>(p->num_seqs) * p->num_kv_heads >= kCombinePerRunMin;
   const size_t slots = static_cast<size_t>(g) + static_cast<size_t>(p->num_seqs) * p->num_kv_heads;
   pl.o_part_bytes = round_up(slots * kGroup * kHeadSize * sizeof(float), kWorkspaceAlign);
   pl.lse_bytes = round_up(slots * kGroup * sizeof(float), kWorkspaceAlign);

@@ -28,6 +28,7 @@ struct Plan {
   bool refetch = false;     // a segment may span more than the walker's 64 page ids
   bool k_rows = false;      // K loaded as whole rows and staged through LDS
   bool ordered = false;     // fixed partitions taken full ones first, tails last
+  bool combine_per_run = false;   // balanced: one combine wave per (sequence, KV head)
   size_t o_part_bytes = 0;
   size_t lse_bytes = 0;
   size_t workspace = 0;

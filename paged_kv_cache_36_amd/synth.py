@@ -84,6 +84,10 @@ WORKLOADS = {
                                       pool_pages=200, seed=4, value_scale=0.5),
     "wide_64seq_b832_p4096": dict(lens="uniform2048_65536", block_size=832,
                                   pool_pages="fit110", seed=5, partition_tokens=4096),
+    # a many-sequence serving batch (beyond the five workloads above): 1024
+    # sequences of 256 to 4096 tokens, the partition size left to the library
+    "serving_1024seq_b832": dict(lens="uniform256_4096x1024", block_size=832,
+                                 pool_pages="fit110", seed=6),
 }
 
 
@@ -98,6 +102,9 @@ def _draw_lens(spec, gen, device):
         return [4096 + edges[i + 1] - edges[i] for i in range(8)]
     if spec == "uniform2048_65536":
         lens = torch.randint(2048, 65536 + 1, (64,), generator=gen, device=device)
+        return [int(x) for x in lens.cpu()]
+    if spec == "uniform256_4096x1024":
+        lens = torch.randint(256, 4096 + 1, (1024,), generator=gen, device=device)
         return [int(x) for x in lens.cpu()]
     return list(spec)
 
@@ -179,13 +186,14 @@ def build_case(name, lens, block_size, pool_pages=None, seed=0, value_scale=1.0,
 
 
 def make_case(name, device="cpu", gen_device=None, seed=None, **over):
-    """Build a named workload. The wide batch draws on the device generator
-    (about 2 x 2.2 G values); all others draw on the CPU generator."""
+    """Build a named workload. The wide and serving batches draw on the device
+    generator (about 2 x 2.2 G values each); all others draw on the CPU
+    generator."""
     spec = dict(WORKLOADS[name])
     if seed is not None:
         spec["seed"] = seed
     if gen_device is None:
-        gen_device = device if name.startswith("wide") else "cpu"
+        gen_device = device if name.startswith(("wide", "serving")) else "cpu"
     spec.update(over)
     return build_case(name, gen_device=gen_device, device=device, **spec)
 

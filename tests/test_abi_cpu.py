@@ -228,7 +228,7 @@ def test_plan_partitions_and_workspace(lib):
         assert 1 <= info.split_workgroups <= min(512, t_max)
         slots = info.split_workgroups + s * 4
         assert info.workspace_bytes >= slots * 6 * 257 * 4 + (s + 1) * 4
-        assert info.combine_workgroups == s * 24 * 4
+        assert info.combine_workgroups == (s * 4 if s * 4 >= 256 else s * 24 * 4)
     # too many sequences for the balanced split: fixed partitions
     st, info = plan(lib, num_seqs=5000, max_seq_len=1024, max_blocks_per_seq=2)
     assert st == 0 and info.balanced == 0
@@ -400,3 +400,12 @@ def test_plan_reports_k_layout_and_dispatch_order(lib):
     assert st == 0 and info.ordered == 0
     st, info = plan(lib, num_seqs=1024, max_seq_len=8192, partition_tokens=512)
     assert st == 0 and info.ordered == 1
+
+
+def test_balanced_combine_takes_one_wave_per_run_for_large_batches(lib):
+    # 64 sequences x 4 KV heads = 256 runs: one combine wave per run
+    st, info = plan(lib, num_seqs=64, max_blocks_per_seq=10, max_seq_len=8192)
+    assert st == 0 and info.balanced == 1 and info.combine_workgroups == 64 * 4
+    # 63 sequences: one wave per (sequence, head, 64 dims)
+    st, info = plan(lib, num_seqs=63, max_blocks_per_seq=10, max_seq_len=8192)
+    assert st == 0 and info.balanced == 1 and info.combine_workgroups == 63 * 24 * 4

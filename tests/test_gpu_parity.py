@@ -373,6 +373,46 @@ def test_fixed_partitions_ordered_dispatch_edge_cases():
         pass
 
 
+def test_fixed_partitions_ordered_at_the_batch_limit():
+    # 1024 sequences, the most the ordered dispatch takes: every thread of a
+    # workgroup scans four lengths
+    rng = np.random.default_rng(83)
+    lens = [int(x) for x in rng.integers(0, 900, size=1024)]
+    case = synth.build_case("ord1024", lens=lens, block_size=832, seed=83, device="cuda")
+    prm = params_of(case, 256)
+    assert pkv.plan(prm)["ordered"] == 1
+    out = run_decode(case, 256)
+    live = [s for s, n in enumerate(lens) if n > 0]
+    ref, _ = oracle_case_parallel(case, seqs=live)
+    assert_bf16_close(out, ref, rows=live, what="ordered 1024 seqs")
+    assert all(np.all(f64(out)[s] == 0) for s, n in enumerate(lens) if n == 0)
+
+
+def test_balanced_split_at_the_batch_limit():
+    # 4096 sequences, the most the balanced split takes (sixteen lengths per
+    # thread in its prefix scan)
+    rng = np.random.default_rng(84)
+    lens = [int(x) for x in rng.integers(0, 200, size=4096)]
+    case = synth.build_case("bal4096", lens=lens, block_size=64, seed=84, device="cuda")
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    out, out32 = run_balanced(case)
+    live = [s for s, n in enumerate(lens) if n > 0]
+    ref, _ = oracle_case_parallel(case, seqs=live)
+    assert_bf16_close(out, ref, rows=live, what="balanced 4096 seqs")
+    assert_rows_rel(f64(out32)[live], ref[live], what="balanced 4096 seqs fp32")
+
+
+def test_serving_batch_every_sequence():
+    # 1024 sequences of 256 to 4096 tokens (2.2 M tokens), the partition size
+    # left to the library (the balanced split)
+    case = synth.make_case("serving_1024seq_b832", device="cuda")
+    assert pkv.plan(params_of(case, 0))["balanced"] == 1
+    out = run_decode(case)
+    ref, _ = oracle_case_parallel(case)
+    assert_bf16_close(out, ref, what="serving batch")
+
+
 def test_fixed_partitions_beyond_the_ordered_limit_use_grid_order():
     rng = np.random.default_rng(82)
     lens = [int(x) for x in rng.integers(1, 700, size=1100)]
@@ -450,12 +490,21 @@ def test_balanced_split_page_size_invariant_bitwise():
         assert np.array_equal(o, outs[0])
 
 
-def test_balanced_split_and_combine_entry_points_match_decode():
-    # the two halves of pkv_decode, called on their own, give its exact bits
-    case = synth.build_case("balhalves", lens=[3000, 1234, 64], block_size=832, seed=65,
-                            device="cuda")
+@pytest.mark.parametrize("nseq", [3, 70])
+def test_balanced_split_and_combine_entry_points_match_decode(nseq):
+    # the two halves of pkv_decode, called on their own, give its exact bits;
+    # 70 sequences (280 runs) take the combine with one wave per run
+    lens = [3000, 1234, 64] if nseq == 3 else [int(x) for x in
+                                               np.random.default_rng(66).integers(1, 2000, nseq)]
+    case = synth.build_case("balhalves", lens=lens, block_size=832, seed=65, device="cuda")
     prm = params_of(case, 0)
-    assert pkv.plan(prm)["balanced"] == 1
+    info = pkv.plan(prm)
+    assert info["balanced"] == 1
+    assert info["combine_workgroups"] == (nseq * 4 if nseq * 4 >= 256 else nseq * 24 * 4)
+    if nseq > 3:
+        ref, _ = oracle_case_parallel(case)
+        out_ref, _ = run_balanced(case)
+        assert_bf16_close(out_ref, ref, what="balanced 70 seqs")
     out, out32 = run_balanced(case)
     ws = torch.empty(pkv.workspace_bytes(prm), dtype=torch.uint8, device="cuda")
     pkv.split_balanced(prm, case.q, case.k_cache, case.v_cache, case.block_table,
