@@ -287,7 +287,8 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
     cold replicas of the state cache. Algorithmic bytes: every window row read
     once (4 KiB: 512 fp32 values + 512 fp32 scores) plus the fp32 output.
     Also times the finalizer alone (RMSNorm, INT8/RoPE packing, KV-page
-    scatter of every output) and the whole operator (both launches)."""
+    scatter of every output), the whole operator as two calls and as one
+    call (pkv_compress_pack, the finalizer fused into the last kernel)."""
     case = synth.make_compress_case(name, device="cuda")
     n, c = case.num_outputs, case.compress_ratio
     rows = sum(min(int(p) + 1, c) for p in case.positions[case.boundaries].tolist())
@@ -326,6 +327,11 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
         step(i)
         finalize(i)
 
+    def pack(i):
+        # the same operator in one call: the finalizer inside the last kernel
+        pkv.compress_pack(caches[i % copies], case.token_to_req, case.positions, case.boundaries,
+                          case.block_table, c, weight, cos_sin, slots, kv, workspace=ws)
+
     def timed(fn):
         with torch.cuda.stream(stream):
             for i in range(warmup):
@@ -347,6 +353,7 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
     us = timed(step)
     us_fin = timed(finalize)
     us_op = timed(operator)
+    us_pack = timed(pack)
     gbps = nbytes / (us * 1e-6) / 1e9
     res = {"workload": name, "kernel": "compress_split_kernel" + ("+compress_combine_kernel"
                                                                  if splits > 1 else ""),
@@ -354,7 +361,8 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
            "num_splits": splits, "workgroups": n * splits, "cold_copies": copies,
            "steps": steps, "algorithmic_bytes": nbytes, "us_per_call": round(us, 3),
            "gbps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
-           "finalize_us": round(us_fin, 3), "operator_us": round(us_op, 3)}
+           "finalize_us": round(us_fin, 3), "operator_us": round(us_op, 3),
+           "pack_us": round(us_pack, 3)}
     log(json.dumps(res))
     del caches, case, out, ws, kv
     torch.cuda.empty_cache()

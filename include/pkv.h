@@ -454,6 +454,31 @@ PKV_API pkv_status pkv_compress_finalize(const pkv_finalize_params* params,
                                          const int64_t* kv_slot_mapping, void* kv_cache,
                                          void* stream);
 
+/* The whole compression operator in one call: pkv_compress followed by
+ * pkv_compress_finalize ("From Attention to KV Cache Compression: Notes from
+ * a KernelGen Optimization", "Our Decomposition": the window reduction, then
+ * the packing of its fp32 rows into KV-cache bytes), with the finalizer run
+ * inside the last kernel on the row that kernel just merged: one launch when
+ * one part covers each window, else the split kernel and a combine that also
+ * packs. Arguments are those of the two calls. params and fparams must agree
+ * on num_outputs, num_tokens and compress_ratio (else PKV_ERR_SHAPE).
+ * `compressed` (fp32 [N, 512], 16-byte aligned) may be NULL; when given it
+ * receives exactly what pkv_compress writes. The kv_cache bytes are exactly
+ * those of pkv_compress then pkv_compress_finalize: an output with a bad
+ * boundary index, request or position packs a NaN row, as it would there, and
+ * one whose slot or RoPE row is out of range writes nothing. Workspace as for
+ * pkv_compress. Asynchronous on `stream`; allocates nothing; host checks
+ * return an error before any launch. */
+PKV_API pkv_status pkv_compress_pack(const pkv_compress_params* params,
+                                     const pkv_finalize_params* fparams,
+                                     const float* state_cache, const int32_t* token_to_req,
+                                     const int64_t* positions,
+                                     const int64_t* boundary_token_indices,
+                                     const int32_t* block_table, const float* rms_norm_weight,
+                                     const float* cos_sin_cache, const int64_t* kv_slot_mapping,
+                                     void* kv_cache, float* compressed, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

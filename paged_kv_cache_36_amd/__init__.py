@@ -4,8 +4,9 @@ The compute path is the HIP library ``libpkv.so`` (C ABI in include/pkv.h);
 ``paged_kv_cache_36_amd.api`` is its thin Python binding. Besides decode, the
 library writes new tokens into the paged cache (``append``), runs the causal
 tail-Q prefill of one sequence (``prefill``), compresses windows of a paged
-state cache and packs the results into KV pages (``compress``,
-``compress_finalize``) and computes the page-size rule (``page_tokens``).
+state cache and packs the results into KV pages (``compress`` and
+``compress_finalize``, or both in one call, ``compress_pack``) and computes
+the page-size rule (``page_tokens``).
 ``synth`` draws the seeded synthetic inputs.
 """
 
@@ -18,6 +19,7 @@ from .api import (  # noqa: F401
     KV_PAGE_BYTES,
     compress,
     compress_finalize,
+    compress_pack,
     compress_params,
     compress_splits,
     compress_workspace_bytes,

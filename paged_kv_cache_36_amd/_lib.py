@@ -136,6 +136,9 @@ SIGNATURES = {
                             _SZ, _VP]),
     "pkv_compress_finalize": (_I32, [ctypes.POINTER(FinalizeParams), _VP, _VP, _VP, _VP, _VP, _VP,
                                      _VP, _VP]),
+    "pkv_compress_pack": (_I32, [ctypes.POINTER(CompressParams), ctypes.POINTER(FinalizeParams),
+                                 _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                 _VP]),
     "pkv_noalloc_scratch_bytes": (_SZ, []),
     "pkv_decode_noalloc": (_I32, [_P, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_probe_sink_floats": (_I32, []),

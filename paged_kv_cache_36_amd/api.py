@@ -427,6 +427,52 @@ def compress_finalize(compressed, positions, boundary_token_indices, rms_norm_we
     return kv_cache
 
 
+def compress_pack(state_cache, token_to_req, positions, boundary_token_indices, block_table,
+                  compress_ratio, rms_norm_weight, cos_sin_cache, kv_slot_mapping, kv_cache,
+                  rms_norm_eps=1.0e-6, *, num_splits=0, compressed=None, workspace=None,
+                  stream=None):
+    """pkv_compress_pack: compress each boundary token's window and pack the
+    rows into kv_cache in one call (the finalizer fused into the last kernel).
+    kv_cache gets the bytes compress() then compress_finalize() would write;
+    ``compressed`` (fp32 [N, 512]), when given, gets compress()'s rows. The
+    workspace is allocated with torch when needed and not given."""
+    for t, name, dt, nd in ((token_to_req, "token_to_req", torch.int32, 1),
+                            (positions, "positions", torch.int64, 1),
+                            (boundary_token_indices, "boundary_token_indices", torch.int64, 1),
+                            (block_table, "block_table", torch.int32, 2),
+                            (rms_norm_weight, "rms_norm_weight", torch.float32, 1),
+                            (cos_sin_cache, "cos_sin_cache", torch.float32, 2),
+                            (kv_slot_mapping, "kv_slot_mapping", torch.int64, 1)):
+        _need(t, name, dt, nd)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _need(kv_cache, "kv_cache", torch.uint8, 2)
+    if kv_cache.stride(1) != 1:
+        raise ValueError("kv_cache pages must be contiguous bytes")
+    if positions.shape[0] != token_to_req.shape[0] or kv_slot_mapping.shape[0] != positions.shape[0]:
+        raise ValueError("token_to_req, positions and kv_slot_mapping differ in length")
+    if rms_norm_weight.shape[0] != 512 or cos_sin_cache.shape[1] != 64:
+        raise ValueError("rms_norm_weight [512], cos_sin_cache [rows, 64]")
+    if compressed is not None:
+        _need(compressed, "compressed", torch.float32, 2)
+    p = compress_params(state_cache, token_to_req, boundary_token_indices, block_table,
+                        compress_ratio, num_splits)
+    fp = _finalize_params(p.num_outputs, positions, cos_sin_cache, kv_cache, compress_ratio,
+                          rms_norm_eps)
+    need = int(load().pkv_compress_workspace_bytes(ctypes.byref(p)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=state_cache.device)
+    _check(load().pkv_compress_pack(ctypes.byref(p), ctypes.byref(fp), _ptr(state_cache),
+                                    _ptr(token_to_req), _ptr(positions),
+                                    _ptr(boundary_token_indices), _ptr(block_table),
+                                    _ptr(rms_norm_weight), _ptr(cos_sin_cache),
+                                    _ptr(kv_slot_mapping), _ptr(kv_cache), _ptr(compressed),
+                                    _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(),
+                                    _stream(stream)), "pkv_compress_pack")
+    return kv_cache
+
+
 def _finalize_params(n, positions, cos_sin_cache, kv_cache, compress_ratio, rms_norm_eps):
     p = FinalizeParams()
     p.num_outputs = n

@@ -590,8 +590,8 @@ bool finalize_pointers_ok(const int64_t* positions, const int64_t* boundary_toke
          aligned(boundary_token_indices, 8) && aligned(kv_slot_mapping, 8);
 }
 
-// Finalizer arguments of a checked call; c comes from `compressed` unless the
-// caller sets the parts fields.
+// Finalizer arguments of a checked call (`compressed` left null: the caller
+// sets it, or the fused path hands the values over inside its last kernel).
 pkv::FinalizeArgs finalize_args(const pkv_finalize_params* p, const int64_t* positions,
                                 const int64_t* boundary_token_indices, const float* rms_norm_weight,
                                 const float* cos_sin_cache, const int64_t* kv_slot_mapping,
@@ -664,6 +664,41 @@ pkv_status pkv_compress_finalize(const pkv_finalize_params* p, const float* comp
                                       cos_sin_cache, kv_slot_mapping, kv_cache);
   a.compressed = compressed;
   return hip_status(pkv::launch_finalize(a, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_compress_pack(const pkv_compress_params* p, const pkv_finalize_params* fp,
+                             const float* state_cache, const int32_t* token_to_req,
+                             const int64_t* positions, const int64_t* boundary_token_indices,
+                             const int32_t* block_table, const float* rms_norm_weight,
+                             const float* cos_sin_cache, const int64_t* kv_slot_mapping,
+                             void* kv_cache, float* compressed, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!p || !fp) return PKV_ERR_NULL;
+  const int32_t s = compress_splits(p);
+  if (s < 0) return static_cast<pkv_status>(s);
+  const pkv_status st = check_finalize_params(fp);
+  if (st != PKV_OK) return st;
+  // both halves describe the same outputs, tokens and window length
+  if (fp->num_outputs != p->num_outputs || fp->num_tokens != p->num_tokens ||
+      fp->compress_ratio != p->compress_ratio)
+    return PKV_ERR_SHAPE;
+  if (p->num_outputs == 0) return PKV_OK;
+  if (!state_cache || !token_to_req || !block_table || !aligned(state_cache, 16) ||
+      !aligned(token_to_req, 4) || !aligned(block_table, 4) ||
+      (compressed && !aligned(compressed, 16)) ||
+      !finalize_pointers_ok(positions, boundary_token_indices, rms_norm_weight, cos_sin_cache,
+                            kv_slot_mapping, kv_cache))
+    return PKV_ERR_NULL;
+  const size_t need = pkv_compress_workspace_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+    return PKV_ERR_WORKSPACE;
+  const pkv::CompressArgs a = compress_args(p, s, state_cache, token_to_req, positions,
+                                            boundary_token_indices, block_table, compressed,
+                                            workspace, need);
+  const pkv::FinalizeArgs f = finalize_args(fp, positions, boundary_token_indices,
+                                            rms_norm_weight, cos_sin_cache, kv_slot_mapping,
+                                            kv_cache);
+  return hip_status(pkv::launch_compress_pack(a, f, static_cast<hipStream_t>(stream)));
 }
 
 int32_t pkv_page_tokens(int64_t state_page_bytes, int64_t attn_bytes_per_token,

@@ -49,8 +49,167 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
-__global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArgs a) {
+// ---------------------------------------------------------------------------
+// Finalizer ("From Attention to KV Cache Compression: Notes from a KernelGen
+// Optimization", "How One Output Is Produced" and "The Finalizer's Sharp
+// Edges"). One wave per output; lane l holds dims 8 l .. 8 l + 7.
+//  - rho = (mean c^2 + eps)^-1/2 (wave sum), y = (c rho) w;
+//  - lanes 0..55 (dims 0..447): z = bf16(y) round trip; group g of 64 dims =
+//    lanes 8 g .. 8 g + 7: a = max(max |z|, 1e-4), e = ceil(log2 fl32(a *
+//    fl32(1/127))) taken exactly from the fp32 exponent and mantissa,
+//    q = trunc(z 2^-e) clipped to [-127, 127], stored as a byte;
+//  - lanes 56..63 (dims 448..511): GPT-J pairs (y[448 + 2j], y[449 + 2j])
+//    rotated by row (p / C) * C of cos_sin (cos j, sin 32 + j), stored bf16;
+//  - the slot's page gets payload [448 INT8][64 bf16] at (slot % 64) * 576
+//    and scale bytes [7 x (e + 127)][0] at 64 * 576 + (slot % 64) * 8.
+// An output whose boundary index, slot or RoPE row is out of range writes
+// nothing.
+// ---------------------------------------------------------------------------
+constexpr int kFinThreads = 256;
+constexpr int kNopeLanes = 56;   // 448 dims / 8
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Where output n goes: its slot and RoPE row, or ok = false when its
+// boundary index, slot or RoPE row is out of range. Uniform over the wave
+// (and the workgroup).
+struct FinIndex {
+  bool ok;
+  int64_t slot;
+  int64_t pc;
+};
+
+__device__ __forceinline__ FinIndex fin_index(const FinalizeArgs& a, int n) {
+  FinIndex ix = {false, 0, 0};
+  const int64_t b = a.boundaries[n];
+  if (b < 0 || b >= a.num_tokens) return ix;
+  const int64_t slot = a.slots[b];
+  const int64_t p = a.positions[b];
+  if (slot < 0 || slot >= a.num_kv_pages * kKvBlockSize || p < 0) return ix;
+  const int64_t pc = (p / a.compress_ratio) * a.compress_ratio;
+  if (pc >= a.cos_sin_rows) return ix;
+  return FinIndex{true, slot, pc};
+}
+
+// The finalizer of one output whose index checks passed, on its compressed
+// values c (lane l: dims 8 l .. 8 l + 7); all 64 lanes of the wave take part.
+__device__ __forceinline__ void fin_write(const FinalizeArgs& a, const FinIndex& ix, int lane,
+                                          const float (&c)[8]) {
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane + 4);
+  const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sq = __builtin_fmaf(c[i], c[i], sq);
+  const float mean = wave_sum(sq) * (1.f / kCompressDim);
+  const float rho = __builtin_amdgcn_rsqf(mean + a.eps);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = (c[i] * rho) * w[i];
+
+  uint8_t* page = a.kv + (ix.slot / kKvBlockSize) * a.kv_page_stride;
+  const int off = static_cast<int>(ix.slot % kKvBlockSize);
+  uint8_t* payload = page + off * kKvTokenStride;
+
+  // NOPE: the group max is taken over all lanes (RoPE lanes join with 0 and
+  // their own group result is unused)
+  float z[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    z[i] = __uint_as_float(bf16_bits(y[i]) << 16);
+    amax = fmaxf(amax, fabsf(z[i]));
+  }
+  if (lane >= kNopeLanes) amax = 0.f;
+#pragma unroll
+  for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float av = fmaxf(amax, 1.0e-4f);
+  const float yq = av * (1.0f / 127.0f);
+  int ex;
+  const float mant = frexpf(yq, &ex);
+  const int e = mant == 0.5f ? ex - 1 : ex;
+  if (lane < kNopeLanes) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = truncf(ldexpf(z[i], -e));
+      q = fminf(fmaxf(q, -127.f), 127.f);
+      const uint32_t byte = static_cast<uint32_t>(static_cast<int>(q)) & 0xffu;
+      if (i < 4) lo |= byte << (8 * i);
+      else hi |= byte << (8 * (i - 4));
+    }
+    *reinterpret_cast<u32x2*>(payload + 8 * lane) = u32x2{lo, hi};
+  } else {
+    // pairs j = 4 (lane - 56) + k: (u, w) = (y[2k], y[2k + 1]); each rotated
+    // value is one explicit fma over the other rounded product, so every
+    // kernel that inlines the finalizer rounds it the same way
+    const int j0 = 4 * (lane - kNopeLanes);
+    const float* row = a.cos_sin + ix.pc * 64;
+    const f32x4 cs = *reinterpret_cast<const f32x4*>(row + j0);
+    const f32x4 sn = *reinterpret_cast<const f32x4*>(row + 32 + j0);
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float u = y[2 * k], v = y[2 * k + 1];
+      const float ru = __builtin_fmaf(u, cs[k], -(v * sn[k]));
+      const float rv = __builtin_fmaf(v, cs[k], u * sn[k]);
+      packed[k] = bf16_bits(ru) | (bf16_bits(rv) << 16);
+    }
+    *reinterpret_cast<u32x4*>(payload + 8 * kNopeLanes + 16 * (lane - kNopeLanes)) =
+        u32x4{packed[0], packed[1], packed[2], packed[3]};
+  }
+  // scale bytes: exponent of group g sits in lane 8 g
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int g = 0; g < 7; ++g) {
+    const uint32_t byte = static_cast<uint32_t>(__shfl(e, 8 * g) + 127) & 0xffu;
+    if (g < 4) lo |= byte << (8 * g);
+    else hi |= byte << (8 * (g - 4));
+  }
+  if (lane == 0)
+    *reinterpret_cast<u32x2*>(page + kKvBlockSize * kKvTokenStride + off * kKvScaleDim) =
+        u32x2{lo, hi};
+}
+
+// The finalizer of the output whose merged row sits in LDS (512 floats):
+// wave-wide, lane l takes dims 8 l .. 8 l + 7.
+__device__ __forceinline__ void fin_from_lds(const FinalizeArgs& a, const FinIndex& ix, int lane,
+                                             const float* row) {
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(row + 8 * lane);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(row + 8 * lane + 4);
+  const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  fin_write(a, ix, lane, c);
+}
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(FinalizeArgs a) {
+  const int lane = lane_id();
+  const int n = blockIdx.x * (kFinThreads / 64) + wave_id();
+  if (n >= a.num_outputs) return;
+  const FinIndex ix = fin_index(a, n);
+  if (!ix.ok) return;
+  const float* crow = a.compressed + static_cast<int64_t>(n) * kCompressDim + 8 * lane;
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(crow);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(crow + 4);
+  const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  fin_write(a, ix, lane, c);
+}
+
+// kPack: one part per window and the finalizer fused (pkv_compress_pack):
+// the two phase-0 waves leave the merged row in LDS and wave 0 packs it.
+template <bool kPack>
+__global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArgs a, FinalizeArgs f) {
   __shared__ CmpLds lds;
+  __shared__ __attribute__((aligned(16))) float fin_row[kCompressDim];   // kPack only
   const int n = blockIdx.x / a.num_splits;
   const int part = blockIdx.x - n * a.num_splits;
   const int lane = lane_id();
@@ -66,6 +225,9 @@ __global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArg
   const int r = a.token_to_req[bs];
   const int64_t p = a.positions[bs];
   ok = ok && r >= 0 && r < a.num_reqs && p >= 0 && p / a.block_size < a.max_blocks;
+  // the finalizer's slot and RoPE row: scalar loads issued now, used after the loop
+  FinIndex fix = {false, 0, 0};
+  if constexpr (kPack) fix = fin_index(f, n);
 
   // The part's positions [ts, ts + nrows): window rows part * R .. part * R +
   // R - 1. A valid p is below max_blocks * B <= INT32_MAX, so 32 bits hold it.
@@ -190,7 +352,7 @@ __global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArg
     lds.num[half][lane] = f32x4{st.num[0], st.num[1], st.num[2], st.num[3]};
   }
   __syncthreads();
-  if (phase == 1) return;
+  if (phase == 0) {
   const f32x4 m1 = lds.m[half][lane];
   const f32x4 d1 = lds.den[half][lane];
   const f32x4 n1 = lds.num[half][lane];
@@ -212,11 +374,18 @@ __global__ __launch_bounds__(kCmpThreads) void compress_split_kernel(CompressArg
   }
   const int dim = kCmpHalf * half + 4 * lane;
   if (a.num_splits == 1) {
-    *reinterpret_cast<f32x4*>(a.out + static_cast<int64_t>(n) * kCompressDim + dim) = c;
+    if (!kPack || a.out)
+      *reinterpret_cast<f32x4*>(a.out + static_cast<int64_t>(n) * kCompressDim + dim) = c;
+    if constexpr (kPack) *reinterpret_cast<f32x4*>(fin_row + dim) = c;
   } else {
     const int64_t idx = (static_cast<int64_t>(n) * a.num_splits + part) * kCompressDim + dim;
     *reinterpret_cast<f32x4*>(a.o_part + idx) = c;
     *reinterpret_cast<f32x4*>(a.lse_part + idx) = lse;
+  }
+  }
+  if constexpr (kPack) {
+    __syncthreads();
+    if (w == 0 && fix.ok) fin_from_lds(f, fix, lane, fin_row);
   }
 }
 
@@ -252,6 +421,8 @@ __device__ __forceinline__ f32x4 shfl_xor4(const f32x4& v, int mask) {
 // its loads in flight at once, and the G lanes then merge with xor shuffles:
 // c = sum_p 2^(lse_p - LSE) c_p / sum_p 2^(lse_p - LSE).
 constexpr int kCmbPartsPerLane = 8;
+// the fused combine's workgroup: 128 (output dims / 4) x at most 8 lanes
+constexpr int kCombinePackMaxThreads = (kCompressDim / 4) * 8;
 
 // Lane g of the combine's merge for one (output, 4 dims): parts 8 g .. 8 g + 7
 // in turn (parts past num_splits merge as empty), from base (the output's
@@ -315,125 +486,33 @@ __global__ __launch_bounds__(kCmpThreads) void compress_combine_kernel(CompressA
   *reinterpret_cast<f32x4*>(a.out + n * kCompressDim + dim) = c;
 }
 
-// ---------------------------------------------------------------------------
-// Finalizer ("From Attention to KV Cache Compression: Notes from a KernelGen
-// Optimization", "How One Output Is Produced" and "The Finalizer's Sharp
-// Edges"). One wave per output; lane l holds dims 8 l .. 8 l + 7.
-//  - rho = (mean c^2 + eps)^-1/2 (wave sum), y = (c rho) w;
-//  - lanes 0..55 (dims 0..447): z = bf16(y) round trip; group g of 64 dims =
-//    lanes 8 g .. 8 g + 7: a = max(max |z|, 1e-4), e = ceil(log2 fl32(a *
-//    fl32(1/127))) taken exactly from the fp32 exponent and mantissa,
-//    q = trunc(z 2^-e) clipped to [-127, 127], stored as a byte;
-//  - lanes 56..63 (dims 448..511): GPT-J pairs (y[448 + 2j], y[449 + 2j])
-//    rotated by row (p / C) * C of cos_sin (cos j, sin 32 + j), stored bf16;
-//  - the slot's page gets payload [448 INT8][64 bf16] at (slot % 64) * 576
-//    and scale bytes [7 x (e + 127)][0] at 64 * 576 + (slot % 64) * 8.
-// An output whose boundary index, slot or RoPE row is out of range writes
-// nothing.
-// ---------------------------------------------------------------------------
-constexpr int kFinThreads = 256;
-constexpr int kNopeLanes = 56;   // 448 dims / 8
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__global__ __launch_bounds__(kFinThreads) void finalize_kernel(FinalizeArgs a) {
-  const int lane = lane_id();
-  const int n = blockIdx.x * (kFinThreads / 64) + wave_id();
-  if (n >= a.num_outputs) return;
-  const int64_t b = a.boundaries[n];
-  if (b < 0 || b >= a.num_tokens) return;
-  const int64_t slot = a.slots[b];
-  const int64_t p = a.positions[b];
-  if (slot < 0 || slot >= a.num_kv_pages * kKvBlockSize || p < 0) return;
-  const int64_t pc = (p / a.compress_ratio) * a.compress_ratio;
-  if (pc >= a.cos_sin_rows) return;
-
-  const float* crow = a.compressed + static_cast<int64_t>(n) * kCompressDim + 8 * lane;
-  const f32x4 c0 = *reinterpret_cast<const f32x4*>(crow);
-  const f32x4 c1 = *reinterpret_cast<const f32x4*>(crow + 4);
-  const f32x4 w0 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane);
-  const f32x4 w1 = *reinterpret_cast<const f32x4*>(a.weight + 8 * lane + 4);
-  float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-  const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-  float sq = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sq = __builtin_fmaf(c[i], c[i], sq);
-  const float mean = wave_sum(sq) * (1.f / kCompressDim);
-  const float rho = __builtin_amdgcn_rsqf(mean + a.eps);
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = (c[i] * rho) * w[i];
-
-  uint8_t* page = a.kv + (slot / kKvBlockSize) * a.kv_page_stride;
-  const int off = static_cast<int>(slot % kKvBlockSize);
-  uint8_t* payload = page + off * kKvTokenStride;
-
-  // NOPE: the group max is taken over all lanes (RoPE lanes join with 0 and
-  // their own group result is unused)
-  float z[8];
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    z[i] = __uint_as_float(bf16_bits(y[i]) << 16);
-    amax = fmaxf(amax, fabsf(z[i]));
+// The combine with the finalizer fused (pkv_compress_pack, several parts per
+// window): one workgroup of 128 G threads per output (G = a.combine_lanes),
+// each (4-dimension group, lane) merging the same parts in the same order as
+// compress_combine_kernel, so the merged row is bit for bit that kernel's;
+// the row goes through LDS to wave 0, which packs it. The finalizer's slot
+// and RoPE row are loaded before the parts arrive.
+__global__ __launch_bounds__(kCombinePackMaxThreads) void compress_combine_pack_kernel(
+    CompressArgs a, FinalizeArgs f) {
+  __shared__ __attribute__((aligned(16))) float fin_row[kCompressDim];
+  const int g_lanes = a.combine_lanes;
+  const int n = blockIdx.x;
+  const int t = threadIdx.x;
+  const int group = t / g_lanes;
+  const int pg = t - group * g_lanes;
+  const int dim = 4 * group;
+  const FinIndex fix = fin_index(f, n);
+  const int64_t base = static_cast<int64_t>(n) * a.num_splits * kCompressDim + dim;
+  CmbState x = cmb_lane(a.lse_part, a.o_part, base, pg, a.num_splits);
+  for (int mask = 1; mask < g_lanes; mask <<= 1)
+    cmb_merge(x, shfl_xor4(x.m, mask), shfl_xor4(x.tot, mask), shfl_xor4(x.acc, mask));
+  if (pg == 0) {
+    const f32x4 c = cmb_value(x);
+    if (a.out) *reinterpret_cast<f32x4*>(a.out + static_cast<int64_t>(n) * kCompressDim + dim) = c;
+    *reinterpret_cast<f32x4*>(fin_row + dim) = c;
   }
-  if (lane >= kNopeLanes) amax = 0.f;
-#pragma unroll
-  for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  const float av = fmaxf(amax, 1.0e-4f);
-  const float yq = av * (1.0f / 127.0f);
-  int ex;
-  const float mant = frexpf(yq, &ex);
-  const int e = mant == 0.5f ? ex - 1 : ex;
-  if (lane < kNopeLanes) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = truncf(ldexpf(z[i], -e));
-      q = fminf(fmaxf(q, -127.f), 127.f);
-      const uint32_t byte = static_cast<uint32_t>(static_cast<int>(q)) & 0xffu;
-      if (i < 4) lo |= byte << (8 * i);
-      else hi |= byte << (8 * (i - 4));
-    }
-    *reinterpret_cast<u32x2*>(payload + 8 * lane) = u32x2{lo, hi};
-  } else {
-    // pairs j = 4 (lane - 56) + k: (u, w) = (y[2k], y[2k + 1])
-    const int j0 = 4 * (lane - kNopeLanes);
-    const float* row = a.cos_sin + pc * 64;
-    const f32x4 cs = *reinterpret_cast<const f32x4*>(row + j0);
-    const f32x4 sn = *reinterpret_cast<const f32x4*>(row + 32 + j0);
-    uint32_t packed[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float u = y[2 * k], v = y[2 * k + 1];
-      const float ru = u * cs[k] - v * sn[k];
-      const float rv = v * cs[k] + u * sn[k];
-      packed[k] = bf16_bits(ru) | (bf16_bits(rv) << 16);
-    }
-    *reinterpret_cast<u32x4*>(payload + 8 * kNopeLanes + 16 * (lane - kNopeLanes)) =
-        u32x4{packed[0], packed[1], packed[2], packed[3]};
-  }
-  // scale bytes: exponent of group g sits in lane 8 g
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int g = 0; g < 7; ++g) {
-    const uint32_t byte = static_cast<uint32_t>(__shfl(e, 8 * g) + 127) & 0xffu;
-    if (g < 4) lo |= byte << (8 * g);
-    else hi |= byte << (8 * (g - 4));
-  }
-  if (lane == 0)
-    *reinterpret_cast<u32x2*>(page + kKvBlockSize * kKvTokenStride + off * kKvScaleDim) =
-        u32x2{lo, hi};
+  __syncthreads();
+  if (t < 64 && fix.ok) fin_from_lds(f, fix, t, fin_row);
 }
 
 }  // namespace
@@ -441,14 +520,32 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(FinalizeArgs a) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
   if (a.num_outputs <= 0) return hipSuccess;
   const int64_t blocks = static_cast<int64_t>(a.num_outputs) * a.num_splits;
-  hipLaunchKernelGGL(compress_split_kernel, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(kCmpThreads), 0, stream, a);
+  hipLaunchKernelGGL(compress_split_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kCmpThreads), 0, stream, a, FinalizeArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
   const int64_t threads = static_cast<int64_t>(a.num_outputs) * (kCompressDim / 4) * a.combine_lanes;
   const int64_t cblocks = (threads + kCmpThreads - 1) / kCmpThreads;
   hipLaunchKernelGGL(compress_combine_kernel, dim3(static_cast<uint32_t>(cblocks)),
                      dim3(kCmpThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_pack(const CompressArgs& a, const FinalizeArgs& f,
+                                hipStream_t stream) {
+  if (a.num_outputs <= 0) return hipSuccess;
+  if (a.num_splits == 1) {
+    hipLaunchKernelGGL(compress_split_kernel<true>, dim3(static_cast<uint32_t>(a.num_outputs)),
+                       dim3(kCmpThreads), 0, stream, a, f);
+    return hipGetLastError();
+  }
+  const int64_t blocks = static_cast<int64_t>(a.num_outputs) * a.num_splits;
+  hipLaunchKernelGGL(compress_split_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(kCmpThreads), 0, stream, a, f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compress_combine_pack_kernel, dim3(static_cast<uint32_t>(a.num_outputs)),
+                     dim3((kCompressDim / 4) * a.combine_lanes), 0, stream, a, f);
   return hipGetLastError();
 }
 

@@ -169,6 +169,10 @@ struct FinalizeArgs {
   float eps;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t stream);
+// pkv_compress_pack: the compression with the finalizer fused into its last
+// kernel (the split kernel with one part per window, else the combine);
+// f.compressed is unused and a.out may be null.
+hipError_t launch_compress_pack(const CompressArgs& a, const FinalizeArgs& f, hipStream_t stream);
 int32_t probe_sink_floats();
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

@@ -307,6 +307,46 @@ def test_compress_workspace_and_argument_checks(lib):
                             1 << 20, None) == -5                 # workspace not 256-byte aligned
 
 
+def fparams(**kw):
+    p = _lib.FinalizeParams()
+    base = dict(num_outputs=64, num_tokens=300, compress_ratio=128, cos_sin_rows=600,
+                num_kv_pages=4, kv_page_stride=64 * 584, rms_norm_eps=1e-6)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_compress_pack_validates_before_any_launch(lib):
+    fake = ctypes.c_void_p(256)
+    pack = lambda cp, fp, state=fake, comp=None, ws=None, wsb=0, slots=fake: lib.pkv_compress_pack(
+        ctypes.byref(cp) if cp is not None else None, ctypes.byref(fp) if fp is not None else None,
+        state, fake, fake, fake, fake, fake, fake, slots, fake, comp, ws, wsb, None)
+    cp = cparams(num_tokens=300, num_outputs=1024)           # one part per window: no workspace
+    assert lib.pkv_compress_workspace_bytes(ctypes.byref(cp)) == 0
+    fp = fparams(num_outputs=1024)
+    assert pack(None, fp) == -1 and pack(cp, None) == -1
+    # the two halves must describe the same outputs, tokens and window
+    assert pack(cp, fparams(num_outputs=1000)) == -2
+    assert pack(cp, fparams(num_outputs=1024, num_tokens=299)) == -2
+    assert pack(cp, fparams(num_outputs=1024, compress_ratio=256)) == -2
+    # each half's own checks
+    assert pack(cparams(num_tokens=300, num_outputs=1024, head_dim=256), fp) == -6
+    assert pack(cp, fparams(num_outputs=1024, kv_page_stride=64 * 584 - 16)) == -8
+    assert pack(cp, fparams(num_outputs=1024, rms_norm_eps=-1.0)) == -2
+    # pointers: state, the finalizer's inputs, `compressed` only when given
+    assert pack(cp, fp, state=None) == -1
+    assert pack(cp, fp, slots=None) == -1
+    assert pack(cp, fp, comp=ctypes.c_void_p(8)) == -1       # not 16-byte aligned
+    # several parts per window need the workspace
+    cp4, fp4 = cparams(num_tokens=300), fparams()
+    assert lib.pkv_compress_splits(ctypes.byref(cp4)) == 4
+    assert pack(cp4, fp4) == -5
+    assert pack(cp4, fp4, ws=ctypes.c_void_p(16), wsb=1 << 22) == -5
+    # no outputs: nothing to check, nothing launched
+    assert pack(cparams(num_outputs=0, num_tokens=300), fparams(num_outputs=0), state=None) == 0
+
+
 def prefill_params(**kw):
     p = _lib.PrefillParams()
     base = dict(num_q_tokens=1500, num_q_heads=24, num_kv_heads=4, head_size=256, block_size=832,

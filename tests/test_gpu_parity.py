@@ -154,6 +154,34 @@ def test_length_sweep(bsz):
         assert_bf16_close(run_decode(case, ptok), ref, what=f"sweep B={bsz} P={ptok}")
 
 
+def test_one_sequence_in_a_thousand_partitions():
+    # 64-token partitions of a 65 553-token sequence: 1025 partials per
+    # (head) row, the last of 17 tokens, so the combine runs 17 chunks of 64
+    lens = [65536 + 17]
+    case = synth.build_case("parts1025", lens=lens, block_size=832, seed=71, device="cuda")
+    ref, _ = oracle_case(case)
+    prm = params_of(case, 64)
+    assert pkv.plan(prm)["num_partitions"] == 1025
+    out32 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    print("[gpu] one sequence, P=64, 1025 partitions", flush=True)
+    out = run_decode(case, 64, out_f32=out32)
+    assert_rows_rel(f64(out32), ref, what="1025 partitions fp32")
+    assert_bf16_close(out, ref, what="1025 partitions")
+
+
+@pytest.mark.parametrize("bsz", [4096, 16384])
+def test_pages_larger_than_any_partition(bsz):
+    # a page holds several partitions (and, at 16384, a whole sequence or
+    # more): the walkers stay inside one page for many blocks, and the page
+    # stride is 16 M elements at 16384 tokens per page
+    lens = [1, 4095, 4097, 20000, 16384]
+    case = synth.build_case(f"bigpage{bsz}", lens=lens, block_size=bsz, seed=72, device="cuda")
+    ref, _ = oracle_case(case)
+    for ptok in (0, 256, 4096):
+        print(f"[gpu] B={bsz} P={ptok}", flush=True)
+        assert_bf16_close(run_decode(case, ptok), ref, what=f"B={bsz} P={ptok}")
+
+
 def test_partials_and_fp32_output():
     case = synth.build_case("parts", lens=[1, 300, 4097, 5000, 64], block_size=784, seed=31,
                             device="cuda")
