@@ -72,12 +72,36 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+C_TEST_SRC = os.path.join(ROOT, "tests", "c_abi", "pkv_c_abi_test.cpp")
+C_TEST_BIN = os.path.join(ROOT, "tests", "c_abi", "pkv_c_abi_test")
+
+
+def build_c_test(verbose: bool = False) -> str:
+    """The C++ test program of the C ABI (host code only: hipMalloc'd buffers
+    and the library's entry points, no Python), linked against the in-tree
+    libpkv.so. Build the library first."""
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", INCLUDE, C_TEST_SRC, "-o", C_TEST_BIN + ".tmp",
+           "-L", PKG, "-lpkv", "-Wl,-rpath,$ORIGIN/../../paged_kv_cache_36_amd"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        noise = "is not a recognized feature for this target"
+        err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        raise RuntimeError(f"hipcc failed on the C ABI test ({res.returncode}):\n{err}")
+    os.replace(C_TEST_BIN + ".tmp", C_TEST_BIN)
+    return C_TEST_BIN
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--save-temps", default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
     args = ap.parse_args()
     print(build(args.save_temps, args.verbose))
+    print(build_c_test(args.verbose))
 
 
 if __name__ == "__main__":
