@@ -59,7 +59,7 @@ def draw_problem(seed):
     return lens, bsz, ptok, joint, scale
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_decode_problem(seed):
     lens, bsz, ptok, joint, scale = draw_problem(seed)
     print(f"[gpu] random seed={seed}: S={len(lens)} B={bsz} P={ptok} joint={joint} "
