@@ -326,22 +326,28 @@ def test_wide_serving_batch_every_sequence():
 
 # ------------------------------------------------------------ other KV head counts
 
+# finite, different heads made from the case's 4: the rows themselves, their
+# dims reversed, rotated by one, and reversed then rotated by three
+HEAD_TRANSFORMS = [lambda t: t, lambda t: t.flip(-1), lambda t: t.roll(1, -1),
+                   lambda t: t.flip(-1).roll(3, -1)]
+
+
 def heads_variant(case, hkv):
     """The case's pages with hkv KV heads (6 query heads each): the first hkv
-    heads for hkv <= 4; for 8, the 4 heads followed by the same rows with
-    each head's dims reversed (a different, finite head). Returns (q, k_cache,
-    v_cache, keys(s), values(s)) with the same block table."""
+    heads for hkv <= 4; for 8 and 16, the 4 heads followed by transformed
+    copies (HEAD_TRANSFORMS), with q's head groups transformed alike. Returns
+    (q, k_cache, v_cache, keys(s), values(s)) with the same block table."""
     def widen(t):
         if hkv <= 4:
             return t[..., :hkv, :].contiguous()
-        return torch.cat([t, t.flip(-1)], dim=-2).contiguous()
+        return torch.cat([f(t) for f in HEAD_TRANSFORMS[:hkv // 4]], dim=-2).contiguous()
     q = case.q[:, :6 * hkv].contiguous() if hkv <= 4 else torch.cat(
-        [case.q, case.q.flip(-1)], dim=1).contiguous()
+        [f(case.q) for f in HEAD_TRANSFORMS[:hkv // 4]], dim=1).contiguous()
     return (q, widen(case.k_cache), widen(case.v_cache), lambda s: widen(case.keys(s)),
             lambda s: widen(case.values(s)))
 
 
-@pytest.mark.parametrize("hkv", [1, 2, 8])
+@pytest.mark.parametrize("hkv", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("ptok", [0, 256])
 def test_other_kv_head_counts(hkv, ptok):
     # the balanced split (P = 0) and ordered fixed partitions, Hq = 6 Hkv
