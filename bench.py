@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 MAIN = "wide_64seq_b832_p4096"
 EXTRA = ["tiny_l1024_b64", "long_l8192_b832", "long_l16384_b832", "long_l32768_b832",
          "ab_l32768_b784", "ab_l32768_b832", "batched_8seq_t131072_b832",
-         "serving_1024seq_b832"]
+         "wide_64seq_b832_auto", "serving_1024seq_b832"]
 PEAK_GBPS = 8000.0            # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 COLD_BYTES = 1 << 30          # touched bytes the replicas must span

@@ -84,6 +84,10 @@ WORKLOADS = {
                                       pool_pages=200, seed=4, value_scale=0.5),
     "wide_64seq_b832_p4096": dict(lens="uniform2048_65536", block_size=832,
                                   pool_pages="fit110", seed=5, partition_tokens=4096),
+    # the wide batch with the partition size left to the library (its
+    # balanced split): the same draw, the library's own plan
+    "wide_64seq_b832_auto": dict(lens="uniform2048_65536", block_size=832,
+                                 pool_pages="fit110", seed=5),
     # a many-sequence serving batch (beyond the five workloads above): 1024
     # sequences of 256 to 4096 tokens, the partition size left to the library
     "serving_1024seq_b832": dict(lens="uniform256_4096x1024", block_size=832,

@@ -322,6 +322,15 @@ def test_wide_serving_batch_every_sequence():
     assert_bf16_close(out, ref, what="wide")
     worst = assert_rows_rel(f64(out32), ref, what="wide fp32")
     print(f"[gpu] wide: worst fp32 row rel err {worst:.2e}", flush=True)
+    # the same batch with the partition size left to the library: its balanced
+    # split, whose page offsets also pass 2^31 elements
+    prm = params_of(case, 0)
+    assert pkv.plan(prm)["balanced"] == 1
+    out32b = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    outb = run_decode(case, 0, out_f32=out32b)
+    assert_bf16_close(outb, ref, what="wide, balanced")
+    worst = assert_rows_rel(f64(out32b), ref, what="wide, balanced fp32")
+    print(f"[gpu] wide, balanced: worst fp32 row rel err {worst:.2e}", flush=True)
 
 
 # ------------------------------------------------------------ other KV head counts
