@@ -328,12 +328,21 @@ typedef struct {
                                  same log-sum-exp merge as decode's partitions)    */
 } pkv_prefill_params;
 
-/* The key splits a pkv_prefill call with these params makes, or a negative
- * pkv_status for invalid params. Host only. With key_splits = 0: one split
- * while the launch has two or more workgroups per CU (128 queries x 1 head per
- * workgroup, 256 CUs); else the smallest count that gives three, at most 16,
- * keeping every split of the shortest query block at 16 or more 64-key tiles. */
+/* The key splits a pkv_prefill call with these params makes per query block
+ * (the most; see below), or a negative pkv_status for invalid params. Host
+ * only. With key_splits = 0: one split while the launch has two or more
+ * workgroups per CU (128 queries x 1 head per workgroup, 256 CUs); else the
+ * smallest count S that gives three, at most 16, keeping every split of the
+ * shortest query block at 16 or more 64-key tiles; and then, if giving the n
+ * shortest query blocks S - 1 splits (for some n below the block count) makes
+ * the workgroups a whole number of rounds over the CUs, the fewest such n
+ * blocks take S - 1. A caller's key_splits applies to every block. */
 PKV_API int32_t pkv_prefill_key_splits(const pkv_prefill_params* params);
+/* How many of the shortest query blocks take one key split fewer than
+ * pkv_prefill_key_splits in a pkv_prefill call with these params (0 when all
+ * take the same count), or a negative pkv_status for invalid params. Host
+ * only. */
+PKV_API int32_t pkv_prefill_short_blocks(const pkv_prefill_params* params);
 /* Workspace pkv_prefill needs: 0 for one split, else splits * Q * Hq * (D + 1)
  * * 4 bytes (fp32 partials and their log-sum-exps). 0 for invalid params. */
 PKV_API size_t pkv_prefill_workspace_bytes(const pkv_prefill_params* params);

@@ -35,6 +35,7 @@ from .api import (  # noqa: F401
     prefill,
     prefill_key_splits,
     prefill_params,
+    prefill_short_blocks,
     prefill_workspace_bytes,
     probe_copy,
     probe_read,

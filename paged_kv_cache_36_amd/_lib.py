@@ -127,6 +127,7 @@ SIGNATURES = {
     "pkv_append": (_I32, [ctypes.POINTER(AppendParams), _VP, _VP, _VP, _VP, _VP, _VP]),
     "pkv_page_tokens": (_I32, [ctypes.c_int64, ctypes.c_int64, _I32]),
     "pkv_prefill_key_splits": (_I32, [ctypes.POINTER(PrefillParams)]),
+    "pkv_prefill_short_blocks": (_I32, [ctypes.POINTER(PrefillParams)]),
     "pkv_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(PrefillParams)]),
     "pkv_prefill": (_I32, [ctypes.POINTER(PrefillParams), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                            _VP]),

@@ -294,6 +294,14 @@ def prefill_key_splits(params):
     return n
 
 
+def prefill_short_blocks(params):
+    """How many of the shortest query blocks take one key split fewer (raises
+    on invalid params)."""
+    n = load().pkv_prefill_short_blocks(ctypes.byref(params))
+    _check(min(n, 0), "pkv_prefill_short_blocks")
+    return n
+
+
 def prefill_workspace_bytes(params):
     """Workspace bytes pkv_prefill needs for these params (0 for one split)."""
     return int(load().pkv_prefill_workspace_bytes(ctypes.byref(params)))

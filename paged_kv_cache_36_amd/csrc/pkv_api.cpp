@@ -124,6 +124,23 @@ int32_t prefill_key_splits(const pkv_prefill_params* p) {
   return k;
 }
 
+// Query blocks that take one key split fewer than the others: with an
+// automatic count S >= 2, the fewest of the shortest (lowest) blocks that
+// make the workgroup count Hq (nqb S - n) a whole number of rounds over the
+// CUs, if some n < nqb does; 0 otherwise, and when the caller fixed the count.
+// The last round then runs full instead of part empty (Q = 1500, L = 20000:
+// 864 workgroups for 256 CUs with 3 splits everywhere; 768 with 2 splits for
+// the 4 shortest of the 12 blocks).
+int32_t prefill_short_blocks(const pkv_prefill_params* p, int32_t splits) {
+  if (p->key_splits > 0 || splits < 2) return 0;
+  const int64_t nqb = (p->num_q_tokens + kPrefillQueries - 1) / kPrefillQueries;
+  const int64_t cus = pkv::plan_cus();
+  for (int64_t n = 0; n < nqb; ++n)
+    if ((static_cast<int64_t>(p->num_q_heads) * (nqb * splits - n)) % cus == 0)
+      return static_cast<int32_t>(n);
+  return 0;
+}
+
 size_t prefill_workspace(const pkv_prefill_params* p, int32_t splits) {
   if (splits <= 1) return 0;
   return static_cast<size_t>(splits) * p->num_q_tokens * p->num_q_heads *
@@ -446,6 +463,13 @@ int32_t pkv_prefill_key_splits(const pkv_prefill_params* p) {
   return prefill_key_splits(p);
 }
 
+int32_t pkv_prefill_short_blocks(const pkv_prefill_params* p) {
+  if (!p) return PKV_ERR_NULL;
+  const pkv_status st = check_prefill_params(p);
+  if (st != PKV_OK) return st;
+  return prefill_short_blocks(p, prefill_key_splits(p));
+}
+
 size_t pkv_prefill_workspace_bytes(const pkv_prefill_params* p) {
   if (!p || check_prefill_params(p) != PKV_OK) return 0;
   return prefill_workspace(p, prefill_key_splits(p));
@@ -467,6 +491,7 @@ pkv_status pkv_prefill(const pkv_prefill_params* p, const void* q, const void* k
     return PKV_ERR_WORKSPACE;
   pkv::PrefillArgs a;
   a.key_splits = splits;
+  a.short_blocks = prefill_short_blocks(p, splits);
   a.o_part = need > 0 ? static_cast<float*>(workspace) : nullptr;
   a.lse_part = need > 0 ? static_cast<float*>(workspace) +
                               static_cast<int64_t>(splits) * p->num_q_tokens * p->num_q_heads *

@@ -113,8 +113,10 @@ struct PrefillArgs {
   float scale_log2;             // scale * log2(e)
   // key splits: 1 writes out / out_f32 directly; more write per-split partials
   // (o_part fp32 [key_splits, num_q, Hq, D], lse_part fp32 [key_splits, num_q,
-  // Hq] in log2 units) that a second kernel merges into out / out_f32
+  // Hq] in log2 units) that a second kernel merges into out / out_f32; the
+  // short_blocks lowest query blocks use only key_splits - 1 of them
   int32_t key_splits;
+  int32_t short_blocks;         // the lowest query blocks that take key_splits - 1 splits
   float* o_part;
   float* lse_part;
 };

@@ -27,10 +27,12 @@
 // At the end the two key halves of each query group merge through LDS.
 //
 // Key splits. When the query blocks are too few to fill the CUs, each block's
-// tiles are cut into key_splits near-equal ranges, one workgroup each; a
-// workgroup then writes its normalized partial output and log2-sum-exp, and
-// prefill_combine_kernel merges the splits with the same log-sum-exp weights
-// as decode's partitions (split-KV, flash-decoding style).
+// tiles are cut into near-equal ranges, one workgroup each: key_splits ranges,
+// or one fewer for the short_blocks shortest query blocks (so the workgroups
+// can make whole rounds over the CUs); a workgroup then writes its normalized
+// partial output and log2-sum-exp, and prefill_combine_kernel merges the
+// splits with the same log-sum-exp weights as decode's partitions (split-KV,
+// flash-decoding style).
 //
 // LDS layout. A direct load writes 64 consecutive 16-byte slots; a tile is
 // stored as 1 KiB blocks of 8 rows x 8 pieces (128 contiguous bytes of each
@@ -117,13 +119,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// (query head, query block, key split) of workgroup b; false for grid
-// padding. XCD x serves KV head x % hkv, so one L2 sees every request for that
-// head's tiles. Query blocks go out longest first, the splits of one block
-// together.
-__device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int nsplit, int& h, int& qb,
-                                         int& split) {
-  const int per_kv = kGroup * nqb * nsplit;
+// Key splits of query block qb: one fewer for the short_blocks shortest
+// (lowest) blocks.
+__device__ __forceinline__ int splits_of(int qb, int nsplit, int short_blocks) {
+  return qb < short_blocks ? nsplit - 1 : nsplit;
+}
+
+// (query head, query block, key split) of workgroup b and the block's split
+// count; false for grid padding. XCD x serves KV head x % hkv, so one L2 sees
+// every request for that head's tiles. The largest shares go out first, the
+// splits of one block together.
+__device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int nsplit, int short_blocks,
+                                         int& h, int& qb, int& split, int& ns) {
+  const int per_kv = kGroup * (nqb * nsplit - short_blocks);
   int j;
   if (kXcds % hkv == 0) {
     const int x = b % kXcds;
@@ -136,8 +144,20 @@ __device__ __forceinline__ bool block_of(int b, int hkv, int nqb, int nsplit, in
     j = (b / hq) * kGroup;
   }
   const int t = j / kGroup;
-  qb = nqb - 1 - t / nsplit;
-  split = t % nsplit;
+  // the short blocks' nsplit - 1 splits go first (each a larger share of its
+  // block than a longer block's split), then the longer blocks' nsplit splits,
+  // each group longest block first
+  const int short_items = short_blocks * (nsplit - 1);
+  if (t < short_items) {
+    qb = short_blocks - 1 - t / (nsplit - 1);
+    split = t % (nsplit - 1);
+    ns = nsplit - 1;
+  } else {
+    const int u = t - short_items;
+    qb = nqb - 1 - u / nsplit;
+    split = u % nsplit;
+    ns = nsplit;
+  }
   return true;
 }
 
@@ -148,9 +168,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) PrefillLds lds;
   const int hq = a.num_kv_heads * kGroup;
   const int nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
-  int h, qb, split;
-  const int nsplit = kSplit ? a.key_splits : 1;
-  if (!block_of(blockIdx.x, a.num_kv_heads, nqb, nsplit, h, qb, split)) return;
+  int h, qb, split, nsplit;
+  if (!block_of(blockIdx.x, a.num_kv_heads, nqb, kSplit ? a.key_splits : 1,
+                kSplit ? a.short_blocks : 0, h, qb, split, nsplit))
+    return;
   const int g = h / kGroup;
   const int lane = lane_id();
   const int wid = wave_id();
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int block_first = first_pos + q0;             // position of the block's first query
   const int kend = first_pos + min(q0 + kPfQueries, a.num_q);   // keys the block needs
   const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
-  // this workgroup's tiles: split `split` of key_splits near-equal ranges
+  // this workgroup's tiles: split `split` of the block's nsplit near-equal ranges
   const int t_lo = kSplit ? static_cast<int>(static_cast<int64_t>(ntiles) * split / nsplit) : 0;
   const int t_hi =
       kSplit ? static_cast<int>(static_cast<int64_t>(ntiles) * (split + 1) / nsplit) : ntiles;
@@ -478,11 +499,13 @@ __global__ __launch_bounds__(kPfCombineThreads) void prefill_combine_kernel(Pref
   if (row >= static_cast<int64_t>(a.num_q) * hq) return;
   const int d = static_cast<int>(t - row * (kHeadSize / 4)) * 4;
   const int64_t split_rows = static_cast<int64_t>(a.num_q) * hq;
+  const int qb = static_cast<int>(row / hq) / kPfQueries;
+  const int ns = splits_of(qb, a.key_splits, a.short_blocks);   // this query's block
   float mx = -INFINITY;
-  for (int j = 0; j < a.key_splits; ++j) mx = fmaxf(mx, a.lse_part[j * split_rows + row]);
+  for (int j = 0; j < ns; ++j) mx = fmaxf(mx, a.lse_part[j * split_rows + row]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int j = 0; j < a.key_splits; ++j) {
+  for (int j = 0; j < ns; ++j) {
     const float w = exp2_fast(a.lse_part[j * split_rows + row] - mx);   // 0 for an empty split
     den += w;
     acc += w * *reinterpret_cast<const f32x4*>(a.o_part + (j * split_rows + row) * kHeadSize + d);
@@ -503,7 +526,7 @@ __global__ __launch_bounds__(kPfCombineThreads) void prefill_combine_kernel(Pref
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_q <= 0) return hipSuccess;
   const int64_t nqb = (a.num_q + kPfQueries - 1) / kPfQueries;
-  const int64_t per_kv = kGroup * nqb * a.key_splits;
+  const int64_t per_kv = kGroup * (nqb * a.key_splits - a.short_blocks);
   int64_t blocks = static_cast<int64_t>(a.num_kv_heads) * per_kv;
   if (kXcds % a.num_kv_heads == 0) {
     // every XCD gets the same number of slots; slots past a head's list exit

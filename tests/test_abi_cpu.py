@@ -358,23 +358,27 @@ def prefill_params(**kw):
     return p
 
 
-@pytest.mark.parametrize("kw,splits", [
-    # 12 query blocks x 24 heads = 288 workgroups: 3 splits give 864 (3.4 per CU)
-    ({}, 3),
+@pytest.mark.parametrize("kw,splits,short", [
+    # 12 query blocks x 24 heads = 288 workgroups: 3 splits give 864 (3.4 per
+    # CU); 2 splits for the 4 shortest blocks make 768, three whole rounds
+    ({}, 3, 4),
     # 32 blocks x 24 heads = 768 workgroups already: one split
-    (dict(num_q_tokens=4096, seq_len=32768, max_blocks=40), 1),
-    # the shortest block has 2300 + 128 keys = 38 tiles: 2 splits keep 16 each
-    (dict(num_q_tokens=700, seq_len=3000, max_blocks=4), 2),
+    (dict(num_q_tokens=4096, seq_len=32768, max_blocks=40), 1, 0),
+    # the shortest block has 2300 + 128 keys = 38 tiles: 2 splits keep 16
+    # each; 24 (12 - n) is never a multiple of 256
+    (dict(num_q_tokens=700, seq_len=3000, max_blocks=4), 2, 0),
     # one query over 32768 keys: 24 workgroups, 16 splits (the cap)
-    (dict(num_q_tokens=1, seq_len=32768, max_blocks=40), 16),
+    (dict(num_q_tokens=1, seq_len=32768, max_blocks=40), 16, 0),
     # too few tiles to split
-    (dict(num_q_tokens=200, seq_len=1000, max_blocks=2), 1),
-    # the caller's count
-    (dict(key_splits=7), 7),
+    (dict(num_q_tokens=200, seq_len=1000, max_blocks=2), 1, 0),
+    # the caller's count, for every block
+    (dict(key_splits=7), 7, 0),
+    (dict(key_splits=3), 3, 0),
 ])
-def test_prefill_key_split_choice(lib, kw, splits):
+def test_prefill_key_split_choice(lib, kw, splits, short):
     p = prefill_params(**kw)
     assert lib.pkv_prefill_key_splits(ctypes.byref(p)) == splits
+    assert lib.pkv_prefill_short_blocks(ctypes.byref(p)) == short
     need = lib.pkv_prefill_workspace_bytes(ctypes.byref(p))
     expect = 0 if splits == 1 else splits * p.num_q_tokens * 24 * 257 * 4
     assert need == expect

@@ -76,6 +76,22 @@ def test_prefill_medium_full_check():
     check(case, q_new, out, out32)
 
 
+def test_prefill_short_blocks_take_one_split_fewer():
+    # Q = 1500 over L = 4600 keys: 3 key splits per query block, and the 4
+    # shortest of the 12 blocks take 2, so the 768 workgroups make three whole
+    # rounds over 256 CUs; every query row against the oracle
+    print("[gpu] prefill Q=1500 L=4600 B=784, short blocks", flush=True)
+    case, q_new = synth.build_prefill_case("pfs", 1500, 4600, 784, seed=61, device="cuda")
+    prm = pkv.prefill_params(q_new, case.k_cache, case.v_cache, case.block_table[0],
+                             case.lens[0], case.block_size, case.scale)
+    assert pkv.prefill_key_splits(prm) == 3 and pkv.prefill_short_blocks(prm) == 4
+    out, out32 = run_prefill(case, q_new)
+    check(case, q_new, out, out32)
+    # the same queries with 3 splits everywhere agree within the same bounds
+    out3, out32_3 = run_prefill(case, q_new, key_splits=3)
+    check(case, q_new, out3, out32_3)
+
+
 def stratified_rows(nq, per_block, seed):
     """per_block query rows from every 128-query block of the kernel (its
     first, last and 32-query group edges, the rest drawn from the seed); each
