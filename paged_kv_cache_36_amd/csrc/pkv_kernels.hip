@@ -376,6 +376,15 @@ constexpr int kTailBuckets = 64;
 __device__ __forceinline__ int tail_bucket(int r, int P) {   // 1 <= r < P
   return static_cast<int>(static_cast<int64_t>(P - r) * kTailBuckets / P);
 }
+// Live workgroup index of slot b of an ordered grid, or -1 for a slot left
+// empty: the four odd slots of every kOddSkipPeriod-th round of 8.
+__device__ __forceinline__ int ordered_live_index(int b) {
+  const int k = b >> 3, x = b & 7;
+  const bool skip_round = k % kOddSkipPeriod == kOddSkipPeriod - 1;
+  if (skip_round && (x & 1)) return -1;
+  return 8 * k - 4 * (k / kOddSkipPeriod) + (skip_round ? x / 2 : x);
+}
+
 __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full_pref,
                                               int32_t* tail_pref, int32_t* tail_sort,
                                               SplitCoord& c) {
@@ -408,7 +417,8 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
     }
   }
   __syncthreads();
-  int bid = blockIdx.x;
+  const int bid = ordered_live_index(blockIdx.x);
+  if (bid < 0) return false;
   c.g = bid % a.num_kv_heads;
   const int item = bid / a.num_kv_heads;
   const int n_full = full_pref[S];
@@ -813,6 +823,23 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
 // computed by every workgroup from seq_lens; workgroup 0 also stores them for
 // the combine kernel (when a.prefix is set).
 // ---------------------------------------------------------------------------
+// The balanced split's first tile of workgroup w: equal shares of the T tiles,
+// shifted so that odd workgroups (odd XCDs) get 1/kOddShareDiv less and even
+// ones 1/kOddShareDiv more, once the shares hold 16 or more tiles (they then
+// keep 14 or more, so none is empty).
+__device__ __forceinline__ int64_t bal_bound(int64_t w, int64_t T, int64_t G) {
+  if (w >= G) return T;
+  const int64_t shift = T >= 16 * G ? T / kOddShareDiv : 0;
+  return (w * T + (w & 1) * shift + G - 1) / G;
+}
+// the workgroup whose share holds tile u (the unshifted owner, or a neighbour)
+__device__ __forceinline__ int64_t bal_owner(int64_t u, int64_t T, int64_t G) {
+  const int64_t q = u * G / T;
+  if (q > 0 && u < bal_bound(q, T, G)) return q - 1;
+  if (q + 1 < G && u >= bal_bound(q + 1, T, G)) return q + 1;
+  return q;
+}
+
 __device__ __forceinline__ int tiles_of(int seq_len) {
   return (seq_len + kTileTokens - 1) / kTileTokens;
 }
@@ -851,8 +878,8 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
   const int64_t G = min(static_cast<int64_t>(gridDim.x), T);
   const int64_t wg = blockIdx.x;
   if (wg >= G) return;
-  const int64_t u0 = (wg * T + G - 1) / G;
-  const int64_t u1 = ((wg + 1) * T + G - 1) / G;
+  const int64_t u0 = bal_bound(wg, T, G);
+  const int64_t u1 = bal_bound(wg + 1, T, G);
 
   // sequence holding unit u0: the last s with pref[s] <= u0 (uniform search)
   int lo = 0, hi = S;   // pref[lo] <= u0 < pref[hi]
@@ -919,8 +946,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     const int64_t T = a.prefix[a.num_seqs];
     const int64_t G = min(static_cast<int64_t>(a.balanced_grid), T);   // as in the split
     const int64_t u_lo = static_cast<int64_t>(a.prefix[s]) + static_cast<int64_t>(g) * n;
-    const int64_t w_first = n > 0 ? u_lo * G / T : 0;
-    const int64_t w_last = n > 0 ? (u_lo + n - 1) * G / T : -1;
+    const int64_t w_first = n > 0 ? bal_owner(u_lo, T, G) : 0;
+    const int64_t w_last = n > 0 ? bal_owner(u_lo + n - 1, T, G) : -1;
     np_balanced = static_cast<int>(w_last - w_first + 1);
     const int64_t slot0 = w_first + static_cast<int64_t>(s) * a.num_kv_heads + g;
     o_base = (slot0 * kG + (h - g * kG)) * kD;
@@ -1037,8 +1064,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_group_kernel(LaunchAr
   const int64_t T = a.prefix[a.num_seqs];
   const int64_t G = min(static_cast<int64_t>(a.balanced_grid), T);   // as in the split
   const int64_t u_lo = static_cast<int64_t>(a.prefix[s]) + static_cast<int64_t>(g) * n;
-  const int64_t w_first = n > 0 ? u_lo * G / T : 0;
-  const int64_t w_last = n > 0 ? (u_lo + n - 1) * G / T : -1;
+  const int64_t w_first = n > 0 ? bal_owner(u_lo, T, G) : 0;
+  const int64_t w_last = n > 0 ? bal_owner(u_lo + n - 1, T, G) : -1;
   const int np = static_cast<int>(w_last - w_first + 1);
   const int64_t slot0 = w_first + static_cast<int64_t>(s) * a.num_kv_heads + g;
 
@@ -1155,11 +1182,12 @@ namespace {
 
 template <class Op>
 hipError_t launch_fixed(const LaunchArgs& a, bool direct, bool ordered, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
-  if (blocks == 0) return hipSuccess;
+  const int64_t live = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.n_parts;
+  if (live == 0) return hipSuccess;
   const bool refetch = partition_needs_refetch(a.partition_tokens, a.block_size);
   // the ordered coordinates only apply to partials (several partitions)
   ordered = ordered && !direct && a.num_seqs <= kMaxOrderedSeqs;
+  const int64_t blocks = ordered ? ordered_grid(live) : live;
   auto kern = direct ? (refetch ? split_decode_kernel<Op, true, true, false>
                                 : split_decode_kernel<Op, true, false, false>)
             : ordered ? (refetch ? split_decode_kernel<Op, false, true, true>

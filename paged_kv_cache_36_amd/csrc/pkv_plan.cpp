@@ -168,7 +168,9 @@ LaunchArgs base_args(const pkv_decode_params* p, const Plan& pl) {
 }
 
 int64_t split_workgroups(const pkv_decode_params* p, const Plan& pl) {
-  return pl.balanced ? pl.grid : static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * pl.n_parts;
+  if (pl.balanced) return pl.grid;
+  const int64_t live = static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * pl.n_parts;
+  return pl.ordered ? ordered_grid(live) : live;
 }
 
 SplitChoice split_choice(const Plan& pl) {

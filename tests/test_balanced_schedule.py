@@ -2,11 +2,14 @@
 
 The balanced split cuts every (sequence, KV head) into 64-token tiles,
 enumerated as (sequence, head, tile); workgroup w of G = min(grid, T) takes
-tiles [ceil(w T / G), ceil((w + 1) T / G)) and writes one partial per
-(sequence, head) run, at slot w + s * Hkv + g. The combine kernel finds the
-partials of (s, g) as the workgroups floor(u G / T) owning its first and last
-tile. This test replays those formulas on random length mixes and checks that
-every token is covered exactly once, that slots never collide and that the
+tiles [B(w), B(w + 1)) with B(w) = ceil((w T + (w mod 2) d) / G), where
+d = floor(T / 24) once T >= 16 G and 0 below (odd workgroups, which run on the
+odd XCDs, get a share 1/24 smaller, even ones 1/24 larger), and writes one
+partial per (sequence, head) run, at slot w + s * Hkv + g. The combine kernel
+finds the partials of (s, g) as the owners of its first and last tile: the
+unshifted owner floor(u G / T) or its neighbour. This test replays those
+formulas on random length mixes and checks that every token is covered
+exactly once, that no share is empty, that slots never collide and that the
 combine's workgroup range is exactly the set of writers.
 """
 
@@ -21,6 +24,25 @@ def tiles(n):
     return (n + TILE - 1) // TILE
 
 
+ODD_SHARE_DIV = 24
+
+
+def bound(w, T, G):
+    if w >= G:
+        return T
+    shift = T // ODD_SHARE_DIV if T >= 16 * G else 0
+    return (w * T + (w & 1) * shift + G - 1) // G
+
+
+def owner(u, T, G):
+    q = u * G // T
+    if q > 0 and u < bound(q, T, G):
+        return q - 1
+    if q + 1 < G and u >= bound(q + 1, T, G):
+        return q + 1
+    return q
+
+
 def split_schedule(lens, hkv, grid):
     pref = [0]
     for n in lens:
@@ -29,8 +51,8 @@ def split_schedule(lens, hkv, grid):
     G = min(grid, T)
     writes = []          # (w, s, g, t_begin, t_end, slot)
     for w in range(G):
-        u0 = (w * T + G - 1) // G
-        u1 = ((w + 1) * T + G - 1) // G
+        u0 = bound(w, T, G)
+        u1 = bound(w + 1, T, G)
         assert u0 < u1, "empty range"
         lo, hi = 0, len(lens)
         while hi - lo > 1:
@@ -65,8 +87,8 @@ def combine_ranges(lens, hkv, grid, pref, T):
                 out[(s, g)] = []
                 continue
             u_lo = pref[s] + g * n
-            w_first = u_lo * G // T
-            w_last = (u_lo + n - 1) * G // T
+            w_first = owner(u_lo, T, G)
+            w_last = owner(u_lo + n - 1, T, G)
             out[(s, g)] = [w + s * hkv + g for w in range(w_first, w_last + 1)]
     return out
 
