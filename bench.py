@@ -370,9 +370,11 @@ def measure_compress(name, steps, warmup, torch, pkv, synth):
 
 
 def read_probe(torch, pkv, reps=20):
-    """Streaming read of 2 GiB of random bytes (the rate depends on the data:
-    constant bytes read about 7 % faster than random ones, which is what the
-    K/V caches hold)."""
+    """Streaming read of 2 GiB of random bytes. The rate depends on how long the
+    memory has been streaming: on an idle GPU it reads about 5 % faster than
+    after a few seconds of sustained reads (the state the timed decode steps run
+    in, after their off-the-clock replays); the contents of the bytes make no
+    measurable difference."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0)
     buf = torch.randint(0, 256, (2 << 30,), dtype=torch.uint8, device="cuda", generator=gen)
@@ -670,6 +672,10 @@ def main():
             sys.exit(f"unknown workload {name}; choose from {known}")
         print(json.dumps({"workload_only": res}), flush=True)
         return
+    # the streaming-read ceiling before any sustained load (for reference; the
+    # ceiling the decode is compared with is taken after the workloads)
+    probe_idle = read_probe(torch, pkv)
+    log(f"read probe on the idle GPU: {probe_idle} GB/s")
     main_res = measure(MAIN, args.steps, args.warmup, torch, pkv, synth)
     extra = []
     if args.workloads in ("all", "decode"):
@@ -696,7 +702,7 @@ def main():
             compresses.append(measure_compress(name, min(args.steps, 100), args.warmup, torch,
                                                pkv, synth))
     probe = read_probe(torch, pkv)
-    log(f"read probe (2 GiB streaming read of random bytes): {probe} GB/s")
+    log(f"read probe (2 GiB streaming read of random bytes) after the workloads: {probe} GB/s")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     cpu_par = None if args.no_cpu_baseline else cpu_baseline_parallel()
@@ -740,6 +746,7 @@ def main():
         "cpu_baseline_parallel": cpu_par,
         "cpu_baseline_rows": cpu_rows,
         "read_probe_gbps": probe,
+        "read_probe_idle_gbps": probe_idle,
         "workloads": [main_res] + extra,
         "append": appends,
         "prefill": prefills,
