@@ -348,6 +348,7 @@ __device__ __forceinline__ void stream_partition(const LaunchArgs& a, PageWalker
 // Workgroup coordinates of a fixed-partition launch: KV head fastest.
 struct SplitCoord {
   int s, part, g;
+  bool nt;   // stores of this workgroup nontemporal (see run_segment)
 };
 __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
   int bid = blockIdx.x;
@@ -356,6 +357,7 @@ __device__ __forceinline__ SplitCoord split_coord(const LaunchArgs& a) {
   bid /= a.num_kv_heads;
   c.part = bid % a.n_parts;
   c.s = bid / a.n_parts;
+  c.nt = static_cast<int64_t>(blockIdx.x) + a.resident_wgs < gridDim.x;
   return c;
 }
 
@@ -422,6 +424,8 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
   c.g = bid % a.num_kv_heads;
   const int item = bid / a.num_kv_heads;
   const int n_full = full_pref[S];
+  c.nt = static_cast<int64_t>(bid) + a.resident_wgs <
+         static_cast<int64_t>(n_full + tail_pref[S]) * a.num_kv_heads;
   if (item < n_full) {
     // the last s with full_pref[s] <= item (uniform search)
     int lo = 0, hi = S;
@@ -506,6 +510,38 @@ enum SegmentTarget : int {
   kToSlot = 2,         // o_part[slot, h % 6, :], lse_part[slot, h % 6] (balanced split)
 };
 
+// A segment's results with cache policy kPolicy: thread d writes dim d of the
+// six heads' rows (bf16 and fp32 outputs, or fp32 partials) and lane 4 h of
+// wave 0 the log-sum-exp of head h.
+template <int kPolicy>
+__device__ __forceinline__ void store_segment(const LaunchArgs& a, SegmentTarget target, int64_t head0,
+                                              int64_t index, int d, const float (&ov)[kG],
+                                              bool lse_lane, int64_t row0, int lse_off,
+                                              float lse) {
+  auto rsrc = [](const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3);
+  };
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    if (target == kToOutput) {
+      const int64_t row = (head0 + h) * kD;
+      if (a.out)
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(f32_to_bf16(ov[h])),
+                                              rsrc(a.out + row, kD * 2), 2 * d, 0, kPolicy);
+      if (a.out_f32)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[h]), rsrc(a.out_f32 + row, kD * 4),
+                                              4 * d, 0, kPolicy);
+    } else {
+      const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index : index * kG + h;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov[h]), rsrc(a.o_part + prow * kD, kD * 4),
+                                            4 * d, 0, kPolicy);
+    }
+  }
+  if (lse_lane)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), rsrc(a.lse_part + row0, 0x7fffffff),
+                                          lse_off, 0, kPolicy);
+}
+
 // The loads a segment starts with: the wave's page list and its 16 bytes of q.
 // They depend on the segment's first token and a bound on its pages only, so
 // the fixed-partition kernel issues them before its sequence length arrives.
@@ -528,7 +564,8 @@ __device__ __forceinline__ void segment_walker(const LaunchArgs& a, int s, int t
 template <bool kKRows, bool kRefetch>
 __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows>& lds,
                                             SegmentStart& su, int s, int g, int t_begin,
-                                            int t_end, SegmentTarget target, int64_t index) {
+                                            int t_end, SegmentTarget target, int64_t index,
+                                            bool nt) {
   const int lane = lane_id();
   const int w = wave_id();
   const int hq = a.num_kv_heads * kG;
@@ -611,6 +648,14 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows
   // den >= 1: the wave holding the maximum contributes its own weight 1
   const float scale_k = fk * __builtin_amdgcn_rcpf(den);
   const float lse_k = (mx + __log2f(den)) * kLn2;
+  // Store policy (nt, uniform): nontemporal while much of the kernel's
+  // reads still follow, the default otherwise. Under the split's read stream,
+  // results stored with the default (write-back) policy held every later wait,
+  // and the end of the workgroup, back: the wide batch's split ran 2.6 % and
+  // the 1024-sequence batch's (16 segments per workgroup) 5.3 % slower with
+  // them. Stores near the end of the kernel complete sooner with the default
+  // policy (one-round grids ran 0.3 to 2 us slower with nontemporal ones).
+  float ov[kG];
 #pragma unroll
   for (int h = 0; h < kG; ++h) {
     float o = 0.f;
@@ -618,23 +663,19 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows
     for (int ww = 0; ww < kWaves; ++ww)
       o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(scale_k), 4 * h + ww)),
                xv[h][ww], o);
-    if (target == kToOutput) {
-      const int64_t idx = (head0 + h) * kD + d;
-      if (a.out) a.out[idx] = static_cast<uint16_t>(f32_to_bf16(o));
-      if (a.out_f32) a.out_f32[idx] = o;
-    } else {
-      const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index
-                                                  : index * kG + h;
-      a.o_part[prow * kD + d] = o;
-    }
+    ov[h] = o;
   }
   // log-sum-exps: lane 4 h of wave 0 holds head h's
-  if (target != kToOutput && w == 0 && wk == 0 && (lane >> 2) < kG) {
-    const int h = lane >> 2;
-    const int64_t prow = target == kToPartition ? (head0 + h) * a.n_parts + index
-                                                : index * kG + h;
-    a.lse_part[prow] = lse_k;
-  }
+  const bool lse_lane = target != kToOutput && w == 0 && wk == 0 && (lane >> 2) < kG;
+  const int64_t row0 = target == kToPartition ? head0 * a.n_parts + index : index * kG;
+  const int lse_off = 4 * (target == kToPartition ? min(lane >> 2, kG - 1) * a.n_parts
+                                                  : min(lane >> 2, kG - 1));
+  // one branch, then stores of a single policy (buffer stores: the policy is
+  // an immediate; every base is wave-uniform)
+  if (nt)
+    store_segment<kPolicyRows>(a, target, head0, index, d, ov, lse_lane, row0, lse_off, lse_k);
+  else
+    store_segment<0>(a, target, head0, index, d, ov, lse_lane, row0, lse_off, lse_k);
   __syncthreads();   // LDS free for the next segment
 }
 
@@ -675,8 +716,8 @@ struct DecodeOp {
   template <bool kRefetch>
   static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds& lds, SegmentStart& su,
                                                  int s, int g, int t_begin, int t_end,
-                                                 SegmentTarget target, int64_t index) {
-    run_segment<kKRows, kRefetch>(a, lds, su, s, g, t_begin, t_end, target, index);
+                                                 SegmentTarget target, int64_t index, bool nt) {
+    run_segment<kKRows, kRefetch>(a, lds, su, s, g, t_begin, t_end, target, index, nt);
   }
   static __device__ __forceinline__ void empty(const LaunchArgs& a, int s, int g) {
     zero_rows(a, s, g);
@@ -712,7 +753,7 @@ struct DebugResolveOp {
   template <bool kRefetch>
   static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds&, SegmentStart& su,
                                                  int s, int g, int t_begin, int t_end,
-                                                 SegmentTarget, int64_t) {
+                                                 SegmentTarget, int64_t, bool) {
     if (g != a.dbg_kv_head) return;
     const int lane = lane_id();
     const int row_stride = a.num_kv_heads * kD;
@@ -742,7 +783,7 @@ struct DebugGatherOp {
   template <bool kRefetch>
   static __device__ __forceinline__ void segment(const LaunchArgs& a, Lds&, SegmentStart& su,
                                                  int s, int g, int t_begin, int t_end,
-                                                 SegmentTarget, int64_t) {
+                                                 SegmentTarget, int64_t, bool) {
     const int lane = lane_id();
     const int row_stride = a.num_kv_heads * kD;
     const int row_bytes = row_stride * 2;
@@ -808,7 +849,7 @@ __global__ __launch_bounds__(kThreads, 2) void split_decode_kernel(LaunchArgs a)
   }
   const int t_end = min(t_cap, seq_len);
   Op::template segment<kRefetch>(a, lds, su, c.s, c.g, t_begin, t_end,
-                                 kDirect ? kToOutput : kToPartition, c.part);
+                                 kDirect ? kToOutput : kToPartition, c.part, c.nt);
 }
 
 // ---------------------------------------------------------------------------
@@ -840,6 +881,7 @@ __device__ __forceinline__ int64_t bal_owner(int64_t u, int64_t T, int64_t G) {
   return q;
 }
 
+constexpr int64_t kNtShareTiles = 64;
 __device__ __forceinline__ int tiles_of(int seq_len) {
   return (seq_len + kTileTokens - 1) / kTileTokens;
 }
@@ -900,8 +942,13 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
     const int t_begin = tile * kTileTokens;
     const int t_end = min(static_cast<int>(tile + (seg_end - u)) * kTileTokens, seq_len);
     SegmentStart su = Op::begin(a, s, g, t_begin, PageWalker::pages_for(t_end, a.block_size));
+    // every workgroup's share ends at about the same time: nontemporal
+    // stores for all but its last segment, once shares are long (64 tiles or
+    // more; the batched workload's 32-tile shares measured 0.5 us slower with
+    // them)
     Op::template segment<kRefetch>(a, lds, su, s, g, t_begin, t_end, kToSlot,
-                                   wg + static_cast<int64_t>(s) * hkv + g);
+                                   wg + static_cast<int64_t>(s) * hkv + g,
+                                   seg_end < u1 && T >= kNtShareTiles * G);
     u = seg_end;
   }
 }

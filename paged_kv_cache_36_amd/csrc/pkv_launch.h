@@ -61,6 +61,8 @@ struct LaunchArgs {
   int32_t n_parts;
   int32_t max_seq_len;
   int32_t balanced_grid;  // balanced split: workgroups G (0 = fixed partitions)
+  int32_t resident_wgs;   // fixed split: workgroups resident at once (2 per CU); the
+                          // ones dispatched before the last round store nontemporally
   float scale_log2;     // scale * log2(e)
   // debug walks only
   int64_t* dbg_offsets;   // resolve: int64 [S, max_seq_len]

@@ -163,6 +163,7 @@ LaunchArgs base_args(const pkv_decode_params* p, const Plan& pl) {
   a.n_parts = pl.n_parts;
   a.max_seq_len = p->max_seq_len;
   a.balanced_grid = pl.balanced ? pl.grid : 0;
+  a.resident_wgs = static_cast<int32_t>(2 * plan_cus());
   a.scale_log2 = static_cast<float>(static_cast<double>(p->scale) * 1.4426950408889634);
   return a;
 }
