@@ -378,15 +378,6 @@ constexpr int kTailBuckets = 64;
 __device__ __forceinline__ int tail_bucket(int r, int P) {   // 1 <= r < P
   return static_cast<int>(static_cast<int64_t>(P - r) * kTailBuckets / P);
 }
-// Live workgroup index of slot b of an ordered grid, or -1 for a slot left
-// empty: the four odd slots of every kOddSkipPeriod-th round of 8.
-__device__ __forceinline__ int ordered_live_index(int b) {
-  const int k = b >> 3, x = b & 7;
-  const bool skip_round = k % kOddSkipPeriod == kOddSkipPeriod - 1;
-  if (skip_round && (x & 1)) return -1;
-  return 8 * k - 4 * (k / kOddSkipPeriod) + (skip_round ? x / 2 : x);
-}
-
 __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full_pref,
                                               int32_t* tail_pref, int32_t* tail_sort,
                                               SplitCoord& c) {
@@ -419,8 +410,7 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
     }
   }
   __syncthreads();
-  const int bid = ordered_live_index(blockIdx.x);
-  if (bid < 0) return false;
+  const int bid = blockIdx.x;
   c.g = bid % a.num_kv_heads;
   const int item = bid / a.num_kv_heads;
   const int n_full = full_pref[S];
@@ -1234,7 +1224,7 @@ hipError_t launch_fixed(const LaunchArgs& a, bool direct, bool ordered, hipStrea
   const bool refetch = partition_needs_refetch(a.partition_tokens, a.block_size);
   // the ordered coordinates only apply to partials (several partitions)
   ordered = ordered && !direct && a.num_seqs <= kMaxOrderedSeqs;
-  const int64_t blocks = ordered ? ordered_grid(live) : live;
+  const int64_t blocks = live;
   auto kern = direct ? (refetch ? split_decode_kernel<Op, true, true, false>
                                 : split_decode_kernel<Op, true, false, false>)
             : ordered ? (refetch ? split_decode_kernel<Op, false, true, true>

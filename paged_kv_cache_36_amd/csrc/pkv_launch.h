@@ -24,19 +24,12 @@ constexpr int kWaves = 4;        // waves per split workgroup
 constexpr int kTileTokens = kWaveTokens * kWaves;  // 64 tokens per workgroup step
 constexpr int kMaxBalancedSeqs = 4096;             // sequences the balanced split handles
 // The dispatcher deals workgroups to the 8 XCDs round robin (workgroup b to
-// XCD b % 8), and on MI355X the workgroups on odd XCDs stream 5-8 % more
-// slowly than those on even ones (the streaming-read probe and both splits,
-// every box measured). The split grids therefore give odd slots less work:
-// the balanced split a share 1/kOddShareDiv smaller (even ones 1/kOddShareDiv
-// larger), the ordered fixed split leaves the four odd slots of every
-// kOddSkipPeriod-th round of 8 slots empty.
+// XCD b % 8), and on MI355X the balanced split's workgroups on odd XCDs
+// stream 5-8 % more slowly than those on even ones (every box measured). Its
+// odd workgroups therefore get a share 1/kOddShareDiv smaller and even ones a
+// share 1/kOddShareDiv larger. (The fixed-partition grid, which the
+// dispatcher refills as slots free up, measured faster without such a skew.)
 constexpr int kOddShareDiv = 24;
-constexpr int kOddSkipPeriod = 12;
-// Slots of an ordered fixed-partition grid holding `live` workgroups (the
-// skipped slots on top, rounded up).
-inline int64_t ordered_grid(int64_t live) {
-  return live + 4 * ((live + 8 * kOddSkipPeriod - 5) / (8 * kOddSkipPeriod - 4)) + 8;
-}
 constexpr int kMaxOrderedSeqs = 1024;              // sequences the ordered fixed split handles
 
 // Everything a split/combine/debug launch needs, already validated.

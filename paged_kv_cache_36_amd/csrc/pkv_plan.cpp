@@ -170,8 +170,7 @@ LaunchArgs base_args(const pkv_decode_params* p, const Plan& pl) {
 
 int64_t split_workgroups(const pkv_decode_params* p, const Plan& pl) {
   if (pl.balanced) return pl.grid;
-  const int64_t live = static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * pl.n_parts;
-  return pl.ordered ? ordered_grid(live) : live;
+  return static_cast<int64_t>(p->num_seqs) * p->num_kv_heads * pl.n_parts;
 }
 
 SplitChoice split_choice(const Plan& pl) {

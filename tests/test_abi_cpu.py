@@ -433,10 +433,8 @@ def test_plan_reports_k_layout_and_dispatch_order(lib):
     st, info = plan(lib, num_seqs=64, max_blocks_per_seq=79, max_seq_len=65536,
                     partition_tokens=4096)
     assert st == 0 and info.balanced == 0 and info.k_rows == 1 and info.ordered == 1
-    # its grid: 64 x 4 x 16 live slots, plus the odd slots of every 12th round
-    # of 8 left empty (4 per 92 live), rounded up
-    live = 64 * 4 * 16
-    assert info.split_workgroups == live + 4 * ((live + 91) // 92) + 8
+    # its grid: one slot per (sequence, KV head, partition), 64 x 4 x 16
+    assert info.split_workgroups == 64 * 4 * 16
     # a batch with the partition size left to the library: balanced, K rows
     st, info = plan(lib, num_seqs=8, max_blocks_per_seq=40, max_seq_len=32768)
     assert st == 0 and info.balanced == 1 and info.k_rows == 1 and info.ordered == 0

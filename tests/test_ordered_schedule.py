@@ -83,32 +83,3 @@ def test_tail_buckets_span_the_partition():
         assert bucket(p - 1, p) == (1 if p == 64 else 0)
         assert bucket(1, p) == TAIL_BUCKETS - 1
         assert all(0 <= bucket(r, p) < TAIL_BUCKETS for r in range(1, p, max(1, p // 97)))
-
-
-SKIP_PERIOD = 12
-
-
-def live_index(b):
-    k, x = b >> 3, b & 7
-    skip = k % SKIP_PERIOD == SKIP_PERIOD - 1
-    if skip and (x & 1):
-        return -1
-    return 8 * k - 4 * (k // SKIP_PERIOD) + (x // 2 if skip else x)
-
-
-def ordered_grid(live):
-    return live + 4 * ((live + 8 * SKIP_PERIOD - 5) // (8 * SKIP_PERIOD - 4)) + 8
-
-
-@pytest.mark.parametrize("live", [1, 7, 8, 95, 96, 97, 400, 2360, 4096, 70001])
-def test_ordered_slots_skip_odd_xcds_and_cover_every_workgroup(live):
-    idx = [live_index(b) for b in range(ordered_grid(live))]
-    taken = [i for i in idx if 0 <= i < live]
-    assert taken == list(range(live))          # each once, in slot order
-    skipped = [b for b, i in enumerate(idx) if i < 0]
-    assert all(b % 2 == 1 and (b // 8) % SKIP_PERIOD == SKIP_PERIOD - 1 for b in skipped)
-    # odd slots carry 11/12 of the workgroups even ones do
-    odd = sum(1 for b, i in enumerate(idx) if 0 <= i < live and b % 2)
-    even = len(taken) - odd
-    if live >= 96 * 4:
-        assert 0.88 < odd / even < 0.95
