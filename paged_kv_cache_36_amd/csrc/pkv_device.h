@@ -34,6 +34,43 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over lane pairs on the vector ALU, with no LDS round trip (a
+// __shfl_xor compiles to ds_bpermute, which goes through LDS). Both lanes of
+// a pair get op(value of the lower lane, value of the upper lane):
+//  - lanes l and l ^ 32: v_permlane32_swap of x with itself leaves the low
+//    half's values in both halves of one result and the high half's in both
+//    halves of the other;
+//  - lanes l and l ^ 16 (16-lane rows 0/1 and 2/3): v_permlane16_swap, alike;
+//  - lanes l and l ^ 1, l ^ 2: DPP quad permutations.
+// With max and + the results equal those of the shuffles bit for bit (the
+// two operands only change places).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+template <int kCtrl>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
 // Order a wave's own LDS writes before its later LDS reads (and reads before
 // later writes). LDS requests of one wave are served in order, so only the
 // compiler has to be kept from moving them.

@@ -246,8 +246,7 @@ __device__ __forceinline__ void process_block(const RowRegs& kb, const RowRegs& 
     if (t + 4 * j + r >= t_end) sv[r] = -INFINITY;
   }
   float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = max_xor32(max_xor16(bm));
   const float m_new = fmaxf(st.m, bm);
   float pv[4];
   float psum = 0.f;
@@ -598,8 +597,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows
   // merge the four waves' states
   const int n = lane & 15;
   const int j = lane >> 4;
-  float l_tot = st.l + __shfl_xor(st.l, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = add_xor32(add_xor16(st.l));
   float* acc_w = reinterpret_cast<float*>(lds_vw);   // this wave's slice, [kG][kAccStride]
   if (n < kG) {
     if (j == 0) {
@@ -629,12 +627,12 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows
   const int wk = lane & 3;
   const float mk = lds.m[wk][hk];
   const float lk = lds.l[wk][hk];
-  float mx = fmaxf(mk, __shfl_xor(mk, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  float mx = fmaxf(mk, quad_swap<kDppQuadXor1>(mk));
+  mx = fmaxf(mx, quad_swap<kDppQuadXor2>(mx));
   const float fk = exp2_fast(mk - mx);   // 0 for a wave without tokens
   float den = fk * lk;
-  den += __shfl_xor(den, 1);
-  den += __shfl_xor(den, 2);
+  den += quad_swap<kDppQuadXor1>(den);
+  den += quad_swap<kDppQuadXor2>(den);
   // den >= 1: the wave holding the maximum contributes its own weight 1
   const float scale_k = fk * __builtin_amdgcn_rcpf(den);
   const float lse_k = (mx + __log2f(den)) * kLn2;
@@ -1044,8 +1042,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
       x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
       cm = fmaxf(cm, ls[u]);
     }
-    cm = fmaxf(cm, __shfl_xor(cm, 16));   // over the 4 partition lanes
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = max_xor32(max_xor16(cm));   // over the 4 partition lanes
     const float m_new = fmaxf(m_run, cm);
     const float m_ref = m_new == -INFINITY ? 0.f : m_new;   // nothing seen yet: weights 0
     const float rescale = exp2_fast(m_run - m_ref);
@@ -1060,14 +1057,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     m_run = m_new;
   }
   // the 4 partition lanes share m_run: plain sums finish the reduction
-#pragma unroll
-  for (int sh = 16; sh <= 32; sh <<= 1) {
-    den += __shfl_xor(den, sh);
-    acc.x += __shfl_xor(acc.x, sh);
-    acc.y += __shfl_xor(acc.y, sh);
-    acc.z += __shfl_xor(acc.z, sh);
-    acc.w += __shfl_xor(acc.w, sh);
-  }
+  den = add_xor32(add_xor16(den));
+  acc.x = add_xor32(add_xor16(acc.x));
+  acc.y = add_xor32(add_xor16(acc.y));
+  acc.z = add_xor32(add_xor16(acc.z));
+  acc.w = add_xor32(add_xor16(acc.w));
   if (pl != 0) return;
   const f32x4 r = np > 0 ? acc * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t idx = row * kD + 64 * quarter + 4 * dl;

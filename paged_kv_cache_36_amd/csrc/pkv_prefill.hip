@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor32(tmax);
     if constexpr (kFold) tmax *= a.scale_log2;
     if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleLog2)) {   // rare after the first tile
       const float m_new = fmaxf(m, tmax);
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   // The two key halves of a query group merge through LDS (the tiles are
   // done): the second half's wave leaves (m, l, acc) there, the first half's
   // wave rescales both to the larger max and writes the output.
-  lsum += __shfl_xor(lsum, 32);
+  lsum = add_xor32(lsum);
   __syncthreads();
   float* mbuf = lds.merge[w];
   if (kh == 1) {
