@@ -68,9 +68,14 @@ __device__ __forceinline__ f32x4 ld4(const float* p) {
 constexpr int kFinThreads = 256;
 constexpr int kNopeLanes = 56;   // 448 dims / 8
 
+// The sum over the wave, pairs l and l ^ m added for m = 32, 16, ..., 1 in
+// turn (every lane ends with the same bits), on the vector ALU.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  x = add_xor16(add_xor32(x));
+  x += dpp_read<kDppRowRor8>(x);
+  x += dpp_read<kDppRowRor4>(x);
+  x += dpp_read<kDppRowRor2>(x);
+  x += dpp_read<kDppQuadXor1>(x);
   return x;
 }
 
@@ -131,8 +136,10 @@ __device__ __forceinline__ void fin_write(const FinalizeArgs& a, const FinIndex&
     amax = fmaxf(amax, fabsf(z[i]));
   }
   if (lane >= kNopeLanes) amax = 0.f;
-#pragma unroll
-  for (int m = 1; m <= 4; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  // max over each group of 8 lanes (pairs l, l ^ 1, then l ^ 2, then l ^ 4)
+  amax = fmaxf(amax, dpp_read<kDppQuadXor1>(amax));
+  amax = fmaxf(amax, dpp_read<kDppQuadXor2>(amax));
+  amax = fmaxf(amax, dpp_read<kDppHalfMirror>(amax));
   const float av = fmaxf(amax, 1.0e-4f);
   const float yq = av * (1.0f / 127.0f);
   int ex;

@@ -64,10 +64,15 @@ __device__ __forceinline__ float add_xor16(float x) {
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+// DPP sources (each lane reads the lane named, within its 16-lane row)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane l ^ 1
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]: lane l ^ 2
+constexpr int kDppRowRor8 = 0x128;      // row_ror 8: lane l ^ 8
+constexpr int kDppRowRor4 = 0x124;      // row_ror 4: lane l ^ 4 once lanes l and l ^ 8 agree
+constexpr int kDppRowRor2 = 0x122;      // row_ror 2: lane l ^ 2 once lanes l, l ^ 4, l ^ 8 agree
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane l ^ 4 once quads agree
 template <int kCtrl>
-__device__ __forceinline__ float quad_swap(float x) {
+__device__ __forceinline__ float dpp_read(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 

@@ -627,12 +627,12 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& a, SplitLds<kKRows
   const int wk = lane & 3;
   const float mk = lds.m[wk][hk];
   const float lk = lds.l[wk][hk];
-  float mx = fmaxf(mk, quad_swap<kDppQuadXor1>(mk));
-  mx = fmaxf(mx, quad_swap<kDppQuadXor2>(mx));
+  float mx = fmaxf(mk, dpp_read<kDppQuadXor1>(mk));
+  mx = fmaxf(mx, dpp_read<kDppQuadXor2>(mx));
   const float fk = exp2_fast(mk - mx);   // 0 for a wave without tokens
   float den = fk * lk;
-  den += quad_swap<kDppQuadXor1>(den);
-  den += quad_swap<kDppQuadXor2>(den);
+  den += dpp_read<kDppQuadXor1>(den);
+  den += dpp_read<kDppQuadXor2>(den);
   // den >= 1: the wave holding the maximum contributes its own weight 1
   const float scale_k = fk * __builtin_amdgcn_rcpf(den);
   const float lse_k = (mx + __log2f(den)) * kLn2;
