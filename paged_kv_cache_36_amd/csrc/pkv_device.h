@@ -76,6 +76,21 @@ __device__ __forceinline__ float dpp_read(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), on
+// the vector ALU: DPP row shifts by 1, 2, 4 and 8 sum within each 16-lane row
+// (lanes shifted in from outside the row add 0), then row 0's total is
+// broadcast into row 1 and row 2's into row 3 (row_bcast 15), and the total
+// of rows 0-1 into rows 2 and 3 (row_bcast 31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr 4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr 8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast 15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast 31 -> rows 2, 3
+  return x;
+}
+
 // Order a wave's own LDS writes before its later LDS reads (and reads before
 // later writes). LDS requests of one wave are served in order, so only the
 // compiler has to be kept from moving them.

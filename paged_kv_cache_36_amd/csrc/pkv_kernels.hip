@@ -391,21 +391,14 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
       const int len = si < S ? min(max(a.seq_lens[si], 0), a.max_seq_len) : 0;
       int f = len / P;
       int t = (len - f * P) > 0 ? 1 : 0;
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) {
-        const int uf = __shfl_up(f, sh);
-        const int ut = __shfl_up(t, sh);
-        if (lane >= sh) {
-          f += uf;
-          t += ut;
-        }
-      }
+      f = wave_incl_scan(f);
+      t = wave_incl_scan(t);
       if (si < S) {
         full_pref[si + 1] = carry_f + f;
         tail_pref[si + 1] = carry_t + t;
       }
-      carry_f += __shfl(f, 63);
-      carry_t += __shfl(t, 63);
+      carry_f += __builtin_amdgcn_readlane(f, 63);
+      carry_t += __builtin_amdgcn_readlane(t, 63);
     }
   }
   __syncthreads();
@@ -440,17 +433,12 @@ __device__ __forceinline__ bool ordered_coord(const LaunchArgs& a, int32_t* full
     }
     wave_lds_sync();
     const int cnt = tail_sort[lane];
-    int incl = cnt;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const int up = __shfl_up(incl, sh);
-      if (lane >= sh) incl += up;
-    }
+    const int incl = wave_incl_scan(cnt);
     const int start = incl - cnt;
     // the one bucket holding position k, and k's place inside it
     const uint64_t hit = __builtin_amdgcn_ballot_w64(cnt > 0 && start <= k && k < incl);
     const int b = static_cast<int>(__builtin_ctzll(hit));
-    int j = k - __shfl(start, b);
+    int j = k - __builtin_amdgcn_readlane(start, b);
     for (int c0 = 0; c0 < S; c0 += 64) {
       const int si = c0 + lane;
       const int len = si < S ? min(max(a.seq_lens[si], 0), a.max_seq_len) : 0;
@@ -889,13 +877,9 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
     for (int c0 = 0; c0 < S; c0 += 64) {
       const int si = c0 + lane;
       int v = si < S ? hkv * tiles_of(min(max(a.seq_lens[si], 0), a.max_seq_len)) : 0;
-#pragma unroll
-      for (int sh = 1; sh < 64; sh <<= 1) {
-        const int up = __shfl_up(v, sh);
-        if (lane >= sh) v += up;
-      }
+      v = wave_incl_scan(v);
       if (si < S) pref[si + 1] = carry + v;
-      carry += __shfl(v, 63);
+      carry += __builtin_amdgcn_readlane(v, 63);
     }
   }
   __syncthreads();
