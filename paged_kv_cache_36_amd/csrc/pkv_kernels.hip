@@ -929,7 +929,8 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
 // Log-sum-exp combine: o = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M),
 // M = max_p lse_p. One wave per (sequence, query head, quarter of the 256
 // dims): lane l is partition lane l >> 4 (of 4) and dim lane l & 15 (4 dims
-// each). The partitions go in chunks of 64; a chunk's 16 partials and
+// each). The partitions go in chunks of 4 kUnroll (16 or, for rows of at most
+// 16 partials, 4 per lane); a chunk's partials and
 // log-sum-exps per lane are loaded at once, then folded into a running
 // maximum, weight sum and weighted sum that the 4 partition lanes share, so
 // the whole reduction stays inside the wave: no LDS, no barrier.
@@ -937,9 +938,8 @@ __global__ __launch_bounds__(kThreads, 2) void balanced_split_kernel(LaunchArgs 
 constexpr int kCombineThreads = 64;
 constexpr int kCombinePLanes = 4;
 constexpr int kCombineUnroll = 16;
-constexpr int kCombineChunk = kCombinePLanes * kCombineUnroll;   // 64 partitions
 
-template <bool kBalanced>
+template <bool kBalanced, int kUnroll>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) {
   const int lane = lane_id();
   const int hq = a.num_kv_heads * kG;
@@ -1006,11 +1006,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
   float den = 0.f;            // sum of weights exp2(lse2 - m_run), this lane's partitions
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   int np = 0;
-  for (int c0 = 0; c0 < np_load; c0 += kCombineChunk) {
-    f32x4 x[kCombineUnroll];
-    float ls[kCombineUnroll];
+  for (int c0 = 0; c0 < np_load; c0 += kUnroll * kCombinePLanes) {
+    f32x4 x[kUnroll];
+    float ls[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {   // straight-line; p >= np_load reads partial 0
+    for (int u = 0; u < kUnroll; ++u) {   // straight-line; p >= np_load reads partial 0
       const int p = c0 + pl + u * kCombinePLanes;
       const int pc = p < np_load ? p : 0;
       x[u] = *reinterpret_cast<const f32x4*>(op + pc * o_stride);
@@ -1020,7 +1020,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     np = count();
     float cm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {   // partitions past the length hold stale data
+    for (int u = 0; u < kUnroll; ++u) {   // partitions past the length hold stale data
       const bool ok = c0 + pl + u * kCombinePLanes < np;
       ls[u] = ok ? ls[u] * kLog2e : -INFINITY;
       x[u] = ok ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1033,7 +1033,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(LaunchArgs a) 
     den *= rescale;
     acc *= rescale;
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) {
+    for (int u = 0; u < kUnroll; ++u) {
       const float w = exp2_fast(ls[u] - m_ref);
       den += w;
       acc += w * x[u];
@@ -1253,8 +1253,12 @@ hipError_t launch_combine(const LaunchArgs& a, bool balanced, bool per_run, hipS
   }
   const int64_t blocks = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * kG * 4;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(balanced ? combine_kernel<true> : combine_kernel<false>,
-                     dim3(static_cast<uint32_t>(blocks)), dim3(kCombineThreads), 0, stream, a);
+  // fixed partitions: four loads per partition lane when the row has at most
+  // 16 partials (the wide batch's 4096-token partitions), else 16 per chunk
+  auto kern = balanced               ? combine_kernel<true, kCombineUnroll>
+              : a.n_parts <= 4 * kCombinePLanes ? combine_kernel<false, 4>
+                                                : combine_kernel<false, kCombineUnroll>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 
