@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,12 +22,12 @@ LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["pkv_kernels.hip", "pkv_append.hip", "pkv_prefill.hip", "pkv_compress.hip",
            "pkv_noalloc.hip", "pkv_plan.cpp", "pkv_api.cpp"]
 
+# flags of every compile
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fvisibility=hidden",
     # no packed-fp32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -45,29 +46,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpkv.so)")
 
 
-def build(save_temps: str | None = None, verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC]
-    if save_temps:
-        # -save-temps=obj writes beside the output, so build into that folder
-        save_temps = os.path.abspath(save_temps)
-        os.makedirs(save_temps, exist_ok=True)
-        tmp = os.path.join(save_temps, "libpkv.so.tmp")
-        cmd += ["-save-temps=obj", "-o", tmp]
-        cwd = save_temps
-    else:
-        cmd += ["-o", tmp]
-        cwd = PKG
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+_NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd: list[str], cwd: str, what: str, verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+        raise RuntimeError(f"hipcc failed on {what} ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
+
+
+def compile_cmd(src: str, obj: str, save_temps: bool = False) -> list[str]:
+    """The hipcc line that compiles one source of the library to an object."""
+    cmd = [hipcc(), *HIPCC_FLAGS]
+    if save_temps:
+        cmd += ["-save-temps=obj"]
+    return cmd + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def build(save_temps: str | None = None, verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link them into
+    libpkv.so in-tree."""
+    out_dir = os.path.abspath(save_temps) if save_temps else os.path.join(PKG, "_objs")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(out_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1, 8)) as pool:
+        futs = [pool.submit(_run, compile_cmd(s, o, bool(save_temps)), out_dir, s, verbose)
+                for s, o in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], PKG,
+         "the link", verbose)
     os.replace(tmp, LIB)
     return LIB
 
