@@ -298,6 +298,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     // chunk by chunk (keys 16 c .. 16 c + 15 = registers 8 c .. 8 c + 7): the
     // second chunk's exponentials can run under the first chunk's products
     const char* vbase = st.v + (4 * kh) * 4 * kBlockBytes;
+    // V^T fragment of step i = 8 c + db (chunk c, dim block db); each is read
+    // two steps ahead of its product (a ring of three), so a product no
+    // longer waits on the transposing reads issued right before it
+    auto read_vt = [&](int i) {
+      // key group of chunk c, read hi: 4 kh + 2 c + hi; piece group db / 2
+      const int c = i >> 3, db = i & 7;
+      const char* vc = vbase + (db & 1 ? v_lane1 : v_lane0) + (db >> 1) * kBlockBytes +
+                       (2 * c) * 4 * kBlockBytes;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vc);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vc + 4 * kBlockBytes));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vq[3];
+    vq[0] = read_vt(0);
+    vq[1] = read_vt(1);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float p[8];
@@ -312,16 +327,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
       const u32x4 packed = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                             pack_bf16(p[6], p[7])};
       const bf16x8 pb = as_bf16x8(packed);
-      // key group of chunk c, read hi: 4 kh + 2 c + hi; piece group db / 2
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const char* vc = vbase + (db & 1 ? v_lane1 : v_lane0) + (db >> 1) * kBlockBytes +
-                         (2 * c) * 4 * kBlockBytes;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vc);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vc + 4 * kBlockBytes));
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, acc[db], 0, 0, 0);
+        const int i = 8 * c + db;
+        if (i + 2 < 16) vq[(i + 2) % 3] = read_vt(i + 2);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i % 3], pb, acc[db], 0, 0, 0);
       }
     }
   };
